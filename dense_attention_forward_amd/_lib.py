@@ -1,0 +1,107 @@
+"""ctypes binding of the C ABI declared in include/attn_fwd.h.
+
+Argument marshalling only: torch supplies device buffers and the current
+stream; every step of the attention forward runs in the HIP library. If
+the library is missing the calls raise; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import threading
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+LIB_PATH = PKG / "libattn_fwd.so"
+
+ATTN_OK = 0
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_ALIGN",
+    4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_OVERLAP", 6: "ATTN_ERR_LAUNCH",
+}
+HEAD_DIM = 128
+
+_lock = threading.Lock()
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn_fwd.so (built by dense_attention_forward_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not LIB_PATH.exists():
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m dense_attention_forward_amd.build`")
+            l = ctypes.CDLL(str(LIB_PATH))
+            vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+            l.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp]
+            l.attn_fwd.restype = i
+            l.attn_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f]
+            l.attn_fwd_check.restype = i
+            l.attn_status_str.argtypes = [i]
+            l.attn_status_str.restype = ctypes.c_char_p
+            _lib = l
+        return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def check(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+          B: int, H: int, S: int, D: int, scale: float) -> int:
+    """Host-only argument validation (no device access)."""
+    return lib().attn_fwd_check(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D, scale)
+
+
+def attn_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
+                 B: int, H: int, S: int, D: int, scale: float, stream: int) -> int:
+    """Direct call of the C entry point with raw device pointers; returns the status."""
+    return lib().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D, scale, stream)
+
+
+def default_scale(D: int = HEAD_DIM) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+def forward(q, k, v, scale: float | None = None, out=None, lse=None):
+    """Attention forward on [B, H, S, 128] bf16 CUDA/HIP tensors -> (o bf16, lse fp32 [B, H, S]).
+
+    Enqueued on torch's current stream; does not synchronise."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, S, D]")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    B, H, S, D = q.shape
+    if scale is None:
+        scale = default_scale(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor shaped like q")
+    if lse.dtype != torch.float32 or lse.shape != (B, H, S) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                      B, H, S, D, float(scale), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st))
+    return out, lse

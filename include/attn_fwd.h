@@ -1,0 +1,82 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) dense attention forward.
+ *
+ * Operation (the "B200 attention kernel from scratch to ~SOTA in 60
+ * figures" article, Chapter 1 "ii. Work parallelization" and section B):
+ * for every batch b, head h and query row i,
+ *
+ *     O[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j) * v_j
+ *
+ * dense (no mask), non-causal, bf16 inputs, head_dim 128. The kernel walks
+ * the keys tile by tile with an online softmax (article, Chapter 1 section
+ * B; Chapter 8 for the base-2 exponent with the scale folded in; Chapter
+ * 11 for the lazily skipped rescale), so the S x S score matrix never
+ * exists in memory. It also writes the natural-log log-sum-exp of each
+ * row's softmax denominator, lse[b,h,i] = ln sum_j exp(scale * q_i . k_j),
+ * which the article does not define (it is the quantity a split over keys
+ * needs to merge partial results).
+ *
+ * Layout: q, k, v and o are contiguous row-major [B, H, S, D] arrays of
+ * bf16 (2 bytes each, D innermost); lse is a contiguous [B, H, S] array of
+ * float32. Index arithmetic is 64-bit.
+ *
+ * Ownership: every pointer is a device pointer owned by the caller. The
+ * library allocates nothing, keeps no state between calls and never
+ * synchronises: attn_fwd enqueues one kernel on `stream` and returns.
+ * q, k, v are only read; every element of o and lse is written.
+ *
+ * Errors: each function returns an attn_status code; nothing is printed
+ * and nothing throws. A fault inside the kernel is reported by the HIP
+ * runtime at the caller's next synchronisation on that stream.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum attn_status {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL = 1,       /* a pointer argument is NULL */
+  ATTN_ERR_SHAPE = 2,      /* D != 128, S < 128, S % 128 != 0, B < 1, H < 1, or the
+                              grid (B*H*S/128 workgroups) exceeds the launch limit */
+  ATTN_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
+  ATTN_ERR_SCALE = 4,      /* scale is not finite or not > 0 (the row max is taken
+                              over raw scores and scaled afterwards, which needs a
+                              positive scale) */
+  ATTN_ERR_OVERLAP = 5,    /* o or lse overlaps q, k, v or each other */
+  ATTN_ERR_LAUNCH = 6      /* the HIP runtime rejected the kernel launch */
+};
+
+/*
+ * Dense attention forward.
+ *   q, k, v : bf16 [B,H,S,D] inputs (device, 16-byte aligned, read only)
+ *   o       : bf16 [B,H,S,D] output (device, 16-byte aligned)
+ *   lse     : fp32 [B,H,S] output, natural-log log-sum-exp per query row
+ *   B, H, S : batch, heads, sequence length (queries = keys = S)
+ *   D       : head dimension, must be 128
+ *   scale   : softmax scale applied to q.k, finite and > 0 (usually 1/sqrt(D))
+ *   stream  : hipStream_t to enqueue on; NULL means the default stream
+ * Returns ATTN_OK or an error code; on error nothing is enqueued (except
+ * ATTN_ERR_LAUNCH, where the runtime refused the launch).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int S, int D, float scale, void* stream);
+
+/*
+ * The argument validation of attn_fwd on its own: pure host code that
+ * touches no device memory and needs no GPU. Returns the status attn_fwd
+ * would return before launching.
+ */
+int attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, int B, int H, int S, int D, float scale);
+
+/* A static, human-readable name for a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

@@ -1,0 +1,131 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its
+host-side validation returns the documented codes (no GPU needed: nothing
+here launches a kernel or touches device memory)."""
+import math
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+import torch
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADERS = sorted((ROOT / "include").glob("*.h"))
+
+
+def _ensure_built():
+    from dense_attention_forward_amd import build as b
+    if not b.LIB.exists():
+        b.build()
+    return b.LIB
+
+
+@pytest.fixture(scope="module")
+def lib():
+    _ensure_built()
+    import dense_attention_forward_amd as daf
+    return daf
+
+
+def _declared_functions():
+    names = []
+    for h in HEADERS:
+        text = h.read_text()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(", text, flags=re.M):
+            if m.group(1) not in ("if", "defined"):
+                names.append(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    assert set(_declared_functions()) >= {"attn_fwd", "attn_fwd_check", "attn_status_str"}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(lib.LIB_PATH)], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib.lib(), name) is not None
+
+
+# Fake, aligned, non-overlapping "device" addresses: only compared, never dereferenced.
+B, H, S, D = 2, 3, 256, 128
+NB = B * H * S * D * 2
+Q, K, V, O, L = (0x10000000 + i * 0x1000000 for i in range(5))
+SC = 1.0 / math.sqrt(128)
+
+
+def _check(lib, q=Q, k=K, v=V, o=O, l=L, b=B, h=H, s=S, d=D, scale=SC):
+    return lib.check(q, k, v, o, l, b, h, s, d, scale)
+
+
+def test_check_ok(lib):
+    assert _check(lib) == 0
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "l"])
+def test_check_null(lib, arg):
+    assert _check(lib, **{arg: 0}) == 1
+
+
+@pytest.mark.parametrize("kw", [dict(d=64), dict(d=256), dict(s=100), dict(s=0), dict(s=-128), dict(s=64),
+                                dict(b=0), dict(h=0), dict(b=-1), dict(b=65536, h=65536, s=128)])
+def test_check_shape(lib, kw):
+    assert _check(lib, **kw) == 2
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "o", "l"])
+def test_check_align(lib, arg):
+    base = {"q": Q, "k": K, "v": V, "o": O, "l": L}[arg]
+    assert _check(lib, **{arg: base + 4}) == 3
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1, float("nan"), float("inf"), -float("inf")])
+def test_check_scale(lib, scale):
+    assert _check(lib, scale=scale) == 4
+
+
+@pytest.mark.parametrize("kw", [dict(o=Q), dict(o=K + 4096), dict(l=V + NB - 16), dict(l=O + 16),
+                                dict(o=L - NB + 16)])
+def test_check_overlap(lib, kw):
+    assert _check(lib, **kw) == 5
+
+
+def test_adjacent_buffers_do_not_overlap(lib):
+    assert _check(lib, o=Q + NB) == 0
+    assert _check(lib, l=O + NB) == 0
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = lib.status_str(code)
+        assert isinstance(s, str) and s
+    assert lib.status_str(0) == "ok"
+    assert lib.status_str(99) == "unknown status"
+
+
+def test_attn_fwd_rejects_before_launch(lib):
+    """The launching entry point validates first; a bad call returns the code
+    without any HIP call, so this runs without a GPU."""
+    assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, 64, SC, 0) == 2
+    assert lib.attn_fwd_raw(0, K, V, O, L, B, H, S, D, SC, 0) == 1
+    assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, D, -1.0, 0) == 4
+
+
+def test_python_wrapper_rejects_bad_tensors(lib):
+    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.forward(q, q, q)  # CPU tensors are rejected before any call
+    with pytest.raises(ValueError):
+        lib.forward(q.float(), q, q)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    from dense_attention_forward_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", tmp_path / "absent.so")
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.lib()

@@ -1,0 +1,225 @@
+"""Parity of the HIP kernel (through the C ABI) with the fp64 CPU oracle.
+
+Bar: O max-abs error <= 2e-2 and mean-abs error <= 2e-3 against the
+unrounded fp64 O; LSE relative error <= 1e-3 (denominator max(|lse|, 1)).
+Small shapes and the two smaller workloads are compared element by element
+over the whole output; the 4K/8K/16K workloads run at full size in the
+benchmark's launch configuration and are compared on sampled rows, plus
+properties that hold at any size.
+"""
+import math
+import sys
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import DEFAULT_SCALE, make_inputs, make_random
+
+pytestmark = pytest.mark.gpu
+
+O_MAX, O_MEAN, LSE_REL = 2e-2, 2e-3, 1e-3
+
+
+@pytest.fixture(scope="module")
+def daf():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import dense_attention_forward_amd as m
+    m.lib()  # raises if the library is missing
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run(daf, q, k, v, scale=DEFAULT_SCALE):
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = daf.forward(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu()
+
+
+def _errors(o, lse, o_ref, lse_ref):
+    e = (o.double() - o_ref).abs()
+    rel = (lse.double() - lse_ref).abs() / lse_ref.abs().clamp_min(1.0)
+    return e.max().item(), e.mean().item(), rel.max().item()
+
+
+def _assert_parity(o, lse, o_ref, lse_ref, what):
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all(), f"{what}: non-finite output"
+    mx, mean, rel = _errors(o, lse, o_ref, lse_ref)
+    _say(f"{what}: O max-abs {mx:.3e} mean-abs {mean:.3e} LSE max-rel {rel:.3e}")
+    assert mx <= O_MAX, f"{what}: O max-abs {mx}"
+    assert mean <= O_MEAN, f"{what}: O mean-abs {mean}"
+    assert rel <= LSE_REL, f"{what}: LSE rel {rel}"
+
+
+SMALL = [
+    # (B, H, S, seed, qk_std, v_dist, outlier_frac)
+    (1, 1, 128, 11, 1.0, "normal", 0.0),
+    (1, 1, 256, 12, 1.0, "normal", 0.0),
+    (1, 2, 384, 13, 2.0, "uniform", 0.0),
+    (2, 3, 640, 14, 1.0, "normal", 0.01),   # 30 workgroups: the XCD renumbering has a tail
+    (1, 1, 1024, 15, 2.0, "uniform", 0.0),
+    (3, 1, 896, 16, 1.0, "normal", 0.05),   # 21 workgroups
+]
+
+
+@pytest.mark.parametrize("B,H,S,seed,std,vd,frac", SMALL)
+def test_small_shapes_full(daf, B, H, S, seed, std, vd, frac):
+    _say(f"case small B={B} H={H} S={S} seed={seed}")
+    q, k, v = make_random(B, H, S, 128, seed=seed, qk_std=std, v_dist=vd, outlier_frac=frac)
+    o, lse = _run(daf, q, k, v)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, f"small {B}x{H}x{S}")
+
+
+@pytest.mark.parametrize("name", ["s256", "s1k"])
+def test_workload_full(daf, name):
+    w = workloads.get(name)
+    _say(f"case workload {w.describe()}")
+    q, k, v = make_inputs(w)
+    o, lse = _run(daf, q, k, v, w.scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, w.scale)
+    _assert_parity(o, lse, o_ref, lse_ref, name)
+
+
+def _picks(w, n_random=160, seed=0):
+    gen = torch.Generator().manual_seed(seed)
+    picks = set()
+    for b in range(w.B):
+        for h in range(w.H):
+            for r in (0, 127, 128, w.S // 2, w.S - 129, w.S - 1):
+                picks.add((b, h, r))
+    bs = torch.randint(0, w.B, (n_random,), generator=gen)
+    hs = torch.randint(0, w.H, (n_random,), generator=gen)
+    rs = torch.randint(0, w.S, (n_random,), generator=gen)
+    for b, h, r in zip(bs.tolist(), hs.tolist(), rs.tolist()):
+        picks.add((b, h, r))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("name", ["s4k", "s8k_peaked", "s16k_outliers"])
+def test_workload_sampled(daf, name):
+    w = workloads.get(name)
+    _say(f"case workload {w.describe()} (full size, sampled rows)")
+    q, k, v = make_inputs(w)
+    o, lse = _run(daf, q, k, v, w.scale)
+    # properties over the whole output
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    vmin = v.float().amin(dim=2, keepdim=True)
+    vmax = v.float().amax(dim=2, keepdim=True)
+    of = o.float()
+    assert (of >= vmin - O_MAX).all() and (of <= vmax + O_MAX).all(), "O outside the hull of V"
+    assert (lse > 0).all()
+    picks = _picks(w)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, picks)
+    idx = tuple(torch.tensor(x) for x in zip(*picks))
+    _assert_parity(o[idx], lse[idx], o_ref, lse_ref, f"{name} ({len(picks)} sampled rows)")
+
+
+def test_deterministic(daf):
+    _say("case determinism")
+    q, k, v = make_random(2, 4, 512, 128, seed=21, outlier_frac=0.01)
+    o1, l1 = _run(daf, q, k, v)
+    o2, l2 = _run(daf, q, k, v)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_side_stream_and_full_overwrite(daf):
+    _say("case side stream")
+    q, k, v = make_random(1, 2, 256, 128, seed=22)
+    dev = torch.device("cuda", 0)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    out = torch.full_like(qd, float("nan"))
+    lse = torch.full((1, 2, 256), float("nan"), device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        daf.forward(qd, kd, vd, DEFAULT_SCALE, out=out, lse=lse)
+    s.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(out.cpu(), lse.cpu(), o_ref, lse_ref, "side stream")
+
+
+def test_zero_queries(daf):
+    """Q = 0: every P is exactly 1, O is the mean of V, lse = ln S."""
+    _say("case q=0")
+    _, k, v = make_random(1, 2, 512, 128, seed=23)
+    q = torch.zeros_like(k)
+    o, lse = _run(daf, q, k, v)
+    mean = v.double().mean(dim=2, keepdim=True).expand_as(o)
+    assert (o.double() - mean).abs().max().item() <= 4e-3
+    assert (lse.double() - math.log(512)).abs().max().item() <= 1e-5
+
+
+def test_identical_keys(daf):
+    _say("case identical keys")
+    q, k, v = make_random(1, 1, 384, 128, seed=24)
+    k = k[:, :, :1].expand_as(k).contiguous()
+    o, lse = _run(daf, q, k, v)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, "identical keys")
+    assert (o.double() - v.double().mean(dim=2, keepdim=True)).abs().max().item() <= 4e-3
+
+
+def test_dominant_key(daf):
+    """One key aligned with every query at a huge score takes all the weight."""
+    _say("case dominant key")
+    q, k, v = make_random(1, 1, 512, 128, seed=25)
+    q = torch.ones_like(q)
+    k = k.clone()
+    k[0, 0, 300] = 4.0  # score 512*scale ~ 45 above the rest
+    o, lse = _run(daf, q, k, v)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, "dominant key")
+
+
+@pytest.mark.parametrize("direction", ["rising", "falling", "late_spike"])
+def test_rebase_patterns(daf, direction):
+    """Rising key norms force a rebase on most tiles; falling ones make later
+    P flush to zero; a spike in the last tile forces one late, large rebase."""
+    _say(f"case rebase {direction}")
+    S = 1024
+    q, k, v = make_random(1, 2, S, 128, seed=26)
+    kf = k.float()
+    if direction == "rising":
+        kf = kf * torch.linspace(0.1, 8.0, S).reshape(1, 1, S, 1)
+    elif direction == "falling":
+        kf = kf * torch.linspace(8.0, 0.1, S).reshape(1, 1, S, 1)
+    else:
+        kf[:, :, S - 5] = q.float()[:, :, 0] * 4.0
+    k = kf.to(torch.bfloat16)
+    o, lse = _run(daf, q, k, v)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, f"rebase {direction}")
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.25, 1e-3])
+def test_other_scales(daf, scale):
+    _say(f"case scale {scale}")
+    q, k, v = make_random(1, 2, 256, 128, seed=27)
+    o, lse = _run(daf, q, k, v, scale)
+    o_ref, lse_ref = oracle.attention(q, k, v, scale)
+    _assert_parity(o, lse, o_ref, lse_ref, f"scale {scale}")
+
+
+def test_bad_arguments_raise(daf):
+    _say("case bad arguments")
+    dev = torch.device("cuda", 0)
+    q = torch.zeros((1, 1, 192, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(daf.AttnError) as e:
+        daf.forward(q, q.clone(), q.clone())
+    assert e.value.status == 2
+    q = torch.zeros((1, 1, 128, 128), dtype=torch.bfloat16, device=dev)
+    with pytest.raises(daf.AttnError) as e:
+        daf.forward(q, q.clone(), q.clone(), scale=-1.0)
+    assert e.value.status == 4
+    with pytest.raises(daf.AttnError) as e:
+        daf.forward(q, q.clone(), q.clone(), out=q)
+    assert e.value.status == 5
