@@ -116,6 +116,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the other sequence lengths")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU-baseline sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB three times (the "
+                         "reference reading for the HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -131,6 +134,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     daf.lib()
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20)
+        x = torch.ones(n, dtype=torch.uint8, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
+        return 0
 
     w = workloads.get(args.workload)
     ms, wall, ok = time_workload(daf, torch, w, args.steps, args.warmup)

@@ -17,8 +17,9 @@ LIB_PATH = PKG / "libattn_fwd.so"
 ATTN_OK = 0
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_ALIGN",
-    4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_OVERLAP", 6: "ATTN_ERR_LAUNCH",
+    4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_OVERLAP", 6: "ATTN_ERR_LAUNCH", 7: "ATTN_ERR_VARIANT",
 }
+VARIANT_AUTO, VARIANT_TILE128, VARIANT_PAIR256 = 0, 1, 2
 HEAD_DIM = 128
 
 _lock = threading.Lock()
@@ -43,6 +44,10 @@ def lib() -> ctypes.CDLL:
             vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
             l.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, vp]
             l.attn_fwd.restype = i
+            l.attn_fwd_variant.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, vp]
+            l.attn_fwd_variant.restype = i
+            l.attn_fwd_pick.argtypes = [i, i, i]
+            l.attn_fwd_pick.restype = i
             l.attn_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f]
             l.attn_fwd_check.restype = i
             l.attn_status_str.argtypes = [i]
@@ -62,16 +67,25 @@ def check(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
 
 
 def attn_fwd_raw(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
-                 B: int, H: int, S: int, D: int, scale: float, stream: int) -> int:
+                 B: int, H: int, S: int, D: int, scale: float, stream: int,
+                 variant: int = VARIANT_AUTO) -> int:
     """Direct call of the C entry point with raw device pointers; returns the status."""
-    return lib().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D, scale, stream)
+    if variant == VARIANT_AUTO:
+        return lib().attn_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D, scale, stream)
+    return lib().attn_fwd_variant(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, S, D, scale, variant,
+                                  stream)
+
+
+def pick(B: int, H: int, S: int) -> int:
+    """The kernel variant attn_fwd uses for this shape (host only)."""
+    return lib().attn_fwd_pick(B, H, S)
 
 
 def default_scale(D: int = HEAD_DIM) -> float:
     return 1.0 / math.sqrt(D)
 
 
-def forward(q, k, v, scale: float | None = None, out=None, lse=None):
+def forward(q, k, v, scale: float | None = None, out=None, lse=None, variant: int = VARIANT_AUTO):
     """Attention forward on [B, H, S, 128] bf16 CUDA/HIP tensors -> (o bf16, lse fp32 [B, H, S]).
 
     Enqueued on torch's current stream; does not synchronise."""
@@ -101,7 +115,7 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None):
         raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                      B, H, S, D, float(scale), stream)
+                      B, H, S, D, float(scale), stream, variant)
     if st != ATTN_OK:
         raise AttnError(st, status_str(st))
     return out, lse

@@ -44,8 +44,13 @@ extern "C" int attn_fwd_check(const void* q, const void* k, const void* v, const
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                        int B, int H, int S, int D, float scale, void* stream) {
+extern "C" int attn_fwd_pick(int B, int H, int S) { return attn_detail::pick_variant(B, H, S); }
+
+extern "C" int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int B, int H, int S, int D, float scale, int variant, void* stream) {
+  if (variant != ATTN_VARIANT_AUTO && variant != ATTN_VARIANT_TILE128 &&
+      variant != ATTN_VARIANT_PAIR256)
+    return ATTN_ERR_VARIANT;
   const int status = attn_fwd_check(q, k, v, o, lse, B, H, S, D, scale);
   if (status != ATTN_OK) return status;
   attn_detail::Params p;
@@ -58,8 +63,14 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   p.H = H;
   p.S = S;
   p.scale = scale;
+  p.variant = variant == ATTN_VARIANT_AUTO ? attn_detail::pick_variant(B, H, S) : variant;
   const hipError_t err = attn_detail::launch(p, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int S, int D, float scale, void* stream) {
+  return attn_fwd_variant(q, k, v, o, lse, B, H, S, D, scale, ATTN_VARIANT_AUTO, stream);
 }
 
 extern "C" const char* attn_status_str(int status) {
@@ -71,6 +82,7 @@ extern "C" const char* attn_status_str(int status) {
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_OVERLAP: return "output buffer overlaps another buffer";
     case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    case ATTN_ERR_VARIANT: return "unknown kernel variant";
     default: return "unknown status";
   }
 }

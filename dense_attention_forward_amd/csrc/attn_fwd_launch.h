@@ -15,7 +15,11 @@ struct Params {
   float* lse;
   int B, H, S;
   float scale;
+  int variant;  // ATTN_VARIANT_TILE128 or ATTN_VARIANT_PAIR256 (resolved, never AUTO)
 };
+
+// The variant chosen for a shape when the caller leaves it to the library.
+int pick_variant(int B, int H, int S);
 
 // Enqueues the forward kernel on `stream`; arguments are already validated.
 hipError_t launch(const Params& p, hipStream_t stream);

@@ -46,7 +46,24 @@ enum attn_status {
                               over raw scores and scaled afterwards, which needs a
                               positive scale) */
   ATTN_ERR_OVERLAP = 5,    /* o or lse overlaps q, k, v or each other */
-  ATTN_ERR_LAUNCH = 6      /* the HIP runtime rejected the kernel launch */
+  ATTN_ERR_LAUNCH = 6,     /* the HIP runtime rejected the kernel launch */
+  ATTN_ERR_VARIANT = 7     /* unknown kernel variant */
+};
+
+/*
+ * Kernel variants. All compute the same operation to the same tolerance;
+ * they differ in how work is laid out on the GPU.
+ *   ATTN_VARIANT_AUTO    : what attn_fwd uses (see attn_fwd_pick)
+ *   ATTN_VARIANT_TILE128 : 4-wave workgroups, one 128-row query tile each
+ *   ATTN_VARIANT_PAIR256 : 8-wave workgroups holding two 128-row query
+ *                          tiles of one head that share every K/V tile, the
+ *                          two 4-wave groups phase-shifted so one runs its
+ *                          matrix products while the other runs its softmax
+ */
+enum attn_variant {
+  ATTN_VARIANT_AUTO = 0,
+  ATTN_VARIANT_TILE128 = 1,
+  ATTN_VARIANT_PAIR256 = 2
 };
 
 /*
@@ -63,6 +80,21 @@ enum attn_status {
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S, int D, float scale, void* stream);
+
+/*
+ * attn_fwd with an explicit kernel variant (enum attn_variant); the same
+ * arguments, layout, ownership and errors as attn_fwd, plus
+ * ATTN_ERR_VARIANT for an unknown variant. For tests and tuning.
+ */
+int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int S, int D, float scale, int variant, void* stream);
+
+/*
+ * The variant attn_fwd picks for a shape (pure host code): PAIR256 when the
+ * grid of query-tile pairs is large enough to fill the GPU, else TILE128.
+ * Returns ATTN_VARIANT_TILE128 or ATTN_VARIANT_PAIR256.
+ */
+int attn_fwd_pick(int B, int H, int S);
 
 /*
  * The argument validation of attn_fwd on its own: pure host code that

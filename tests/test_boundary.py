@@ -39,7 +39,8 @@ def _declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert set(_declared_functions()) >= {"attn_fwd", "attn_fwd_check", "attn_status_str"}
+    assert set(_declared_functions()) >= {"attn_fwd", "attn_fwd_check", "attn_status_str",
+                                          "attn_fwd_variant", "attn_fwd_pick"}
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -100,7 +101,7 @@ def test_adjacent_buffers_do_not_overlap(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         s = lib.status_str(code)
         assert isinstance(s, str) and s
     assert lib.status_str(0) == "ok"
@@ -129,3 +130,20 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(_lib, "LIB_PATH", tmp_path / "absent.so")
     with pytest.raises(RuntimeError, match="missing"):
         _lib.lib()
+
+
+def test_variant_rejected_before_launch(lib):
+    for bad in (-1, 3, 99):
+        assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, D, SC, 0, variant=bad) == 7
+    # a valid variant with bad arguments still reports the argument error
+    assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, 64, SC, 0, variant=2) == 2
+
+
+def test_pick(lib):
+    # small grids of query-tile pairs keep one 128-row tile per workgroup
+    assert lib.pick(1, 1, 256) == lib.VARIANT_TILE128
+    assert lib.pick(2, 16, 1024) == lib.VARIANT_TILE128
+    # the 4K/8K/16K workloads fill the GPU with tile pairs
+    assert lib.pick(4, 16, 4096) == lib.VARIANT_PAIR256
+    assert lib.pick(2, 16, 8192) == lib.VARIANT_PAIR256
+    assert lib.pick(1, 16, 16384) == lib.VARIANT_PAIR256

@@ -36,10 +36,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _run(daf, q, k, v, scale=DEFAULT_SCALE):
+VARIANTS = [1, 2]  # TILE128, PAIR256 (forced, whatever attn_fwd would pick)
+
+
+def _run(daf, q, k, v, scale=DEFAULT_SCALE, variant=0):
     dev = torch.device("cuda", 0)
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    o, lse = daf.forward(qd, kd, vd, scale)
+    o, lse = daf.forward(qd, kd, vd, scale, variant=variant)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
 
@@ -70,23 +73,25 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("B,H,S,seed,std,vd,frac", SMALL)
-def test_small_shapes_full(daf, B, H, S, seed, std, vd, frac):
-    _say(f"case small B={B} H={H} S={S} seed={seed}")
+def test_small_shapes_full(daf, B, H, S, seed, std, vd, frac, variant):
+    _say(f"case small B={B} H={H} S={S} seed={seed} variant={variant}")
     q, k, v = make_random(B, H, S, 128, seed=seed, qk_std=std, v_dist=vd, outlier_frac=frac)
-    o, lse = _run(daf, q, k, v)
+    o, lse = _run(daf, q, k, v, variant=variant)
     o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
-    _assert_parity(o, lse, o_ref, lse_ref, f"small {B}x{H}x{S}")
+    _assert_parity(o, lse, o_ref, lse_ref, f"small {B}x{H}x{S} v{variant}")
 
 
+@pytest.mark.parametrize("variant", [0] + VARIANTS)
 @pytest.mark.parametrize("name", ["s256", "s1k"])
-def test_workload_full(daf, name):
+def test_workload_full(daf, name, variant):
     w = workloads.get(name)
-    _say(f"case workload {w.describe()}")
+    _say(f"case workload {w.describe()} variant={variant}")
     q, k, v = make_inputs(w)
-    o, lse = _run(daf, q, k, v, w.scale)
+    o, lse = _run(daf, q, k, v, w.scale, variant=variant)
     o_ref, lse_ref = oracle.attention(q, k, v, w.scale)
-    _assert_parity(o, lse, o_ref, lse_ref, name)
+    _assert_parity(o, lse, o_ref, lse_ref, f"{name} v{variant}")
 
 
 def _picks(w, n_random=160, seed=0):
@@ -106,8 +111,9 @@ def _picks(w, n_random=160, seed=0):
 
 @pytest.mark.parametrize("name", ["s4k", "s8k_peaked", "s16k_outliers"])
 def test_workload_sampled(daf, name):
+    """Full size, in the launch configuration the benchmark times (attn_fwd's own pick)."""
     w = workloads.get(name)
-    _say(f"case workload {w.describe()} (full size, sampled rows)")
+    _say(f"case workload {w.describe()} (full size, sampled rows, variant {daf.pick(w.B, w.H, w.S)})")
     q, k, v = make_inputs(w)
     o, lse = _run(daf, q, k, v, w.scale)
     # properties over the whole output
@@ -123,11 +129,22 @@ def test_workload_sampled(daf, name):
     _assert_parity(o[idx], lse[idx], o_ref, lse_ref, f"{name} ({len(picks)} sampled rows)")
 
 
-def test_deterministic(daf):
-    _say("case determinism")
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_deterministic(daf, variant):
+    _say(f"case determinism variant={variant}")
     q, k, v = make_random(2, 4, 512, 128, seed=21, outlier_frac=0.01)
-    o1, l1 = _run(daf, q, k, v)
-    o2, l2 = _run(daf, q, k, v)
+    o1, l1 = _run(daf, q, k, v, variant=variant)
+    o2, l2 = _run(daf, q, k, v, variant=variant)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_variants_agree(daf):
+    """Both layouts run the same per-row arithmetic in the same order, so
+    they agree bit for bit."""
+    _say("case variants agree")
+    q, k, v = make_random(1, 3, 640, 128, seed=28, qk_std=2.0)
+    o1, l1 = _run(daf, q, k, v, variant=1)
+    o2, l2 = _run(daf, q, k, v, variant=2)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
@@ -147,12 +164,13 @@ def test_side_stream_and_full_overwrite(daf):
     _assert_parity(out.cpu(), lse.cpu(), o_ref, lse_ref, "side stream")
 
 
-def test_zero_queries(daf):
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_zero_queries(daf, variant):
     """Q = 0: every P is exactly 1, O is the mean of V, lse = ln S."""
-    _say("case q=0")
+    _say(f"case q=0 variant={variant}")
     _, k, v = make_random(1, 2, 512, 128, seed=23)
     q = torch.zeros_like(k)
-    o, lse = _run(daf, q, k, v)
+    o, lse = _run(daf, q, k, v, variant=variant)
     mean = v.double().mean(dim=2, keepdim=True).expand_as(o)
     assert (o.double() - mean).abs().max().item() <= 4e-3
     assert (lse.double() - math.log(512)).abs().max().item() <= 1e-5
@@ -180,11 +198,12 @@ def test_dominant_key(daf):
     _assert_parity(o, lse, o_ref, lse_ref, "dominant key")
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("direction", ["rising", "falling", "late_spike"])
-def test_rebase_patterns(daf, direction):
+def test_rebase_patterns(daf, direction, variant):
     """Rising key norms force a rebase on most tiles; falling ones make later
     P flush to zero; a spike in the last tile forces one late, large rebase."""
-    _say(f"case rebase {direction}")
+    _say(f"case rebase {direction} variant={variant}")
     S = 1024
     q, k, v = make_random(1, 2, S, 128, seed=26)
     kf = k.float()
@@ -195,9 +214,9 @@ def test_rebase_patterns(daf, direction):
     else:
         kf[:, :, S - 5] = q.float()[:, :, 0] * 4.0
     k = kf.to(torch.bfloat16)
-    o, lse = _run(daf, q, k, v)
+    o, lse = _run(daf, q, k, v, variant=variant)
     o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
-    _assert_parity(o, lse, o_ref, lse_ref, f"rebase {direction}")
+    _assert_parity(o, lse, o_ref, lse_ref, f"rebase {direction} v{variant}")
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.25, 1e-3])
@@ -223,3 +242,6 @@ def test_bad_arguments_raise(daf):
     with pytest.raises(daf.AttnError) as e:
         daf.forward(q, q.clone(), q.clone(), out=q)
     assert e.value.status == 5
+    with pytest.raises(daf.AttnError) as e:
+        daf.forward(q, q.clone(), q.clone(), variant=5)
+    assert e.value.status == 7
