@@ -47,6 +47,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kD = 128;         // head dimension
@@ -54,6 +58,7 @@ constexpr int kBM = 128;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRebaseLog2 = 8.0f;  // rebase threshold in base-2 exponent units
+constexpr i16x2 kOnesBf16x2 = {0x3f80, 0x3f80};  // bf16 (1.0, 1.0)
 
 // Tile parameters (compile-time): keys per K/V tile and the waves per SIMD
 // the register allocation is held to.
@@ -88,6 +93,18 @@ __device__ __forceinline__ int k_fill_offset(int l) {
 __device__ __forceinline__ int v_fill_offset(int l) {
   const int b = l >> 4, q = (l >> 2) & 3, x = l & 3;
   return q * 256 + (4 * b + x) * 16;
+}
+
+// Base update without touching O: returns the factor O must be multiplied
+// by before the next P.V (1 for rows that keep their base; exactly 1.0, so
+// multiplying by it changes nothing).
+__device__ __forceinline__ float base_update_alpha(float raw_max, float c, float& kept, float& lsum) {
+  const float cand = fmaxf(kept, raw_max * c);
+  const bool need = (cand - kept) >= kRebaseLog2;
+  const float alpha = need ? __builtin_amdgcn_exp2f(kept - cand) : 1.0f;
+  lsum *= alpha;
+  kept = need ? cand : kept;
+  return alpha;
 }
 
 template <int BN>
@@ -136,13 +153,26 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[BN / 32]) {
   return fmaxf(mx, __shfl_xor(mx, 32));
 }
 
-// P = 2^(s*c - kept) as the PV B operand; returns the sum of the unrounded
-// values. Step t's operand: slots 0..3 <- block t/2, j = 2(t%2); slots
-// 4..7 <- j = 2(t%2)+1.
+// acc + x[e] + x[e+1] for bf16 x, with exact products against (1, 1) and
+// an fp32 sum (v_dot2c_f32_bf16). The pair is rebuilt from its elements:
+// with this compiler, pairs taken from a bit-cast of the whole vector were
+// lowered to the same register for different pairs.
+__device__ __forceinline__ float add_bf16_pair(float acc, const bf16x8& x, int e) {
+  bf16x2 pair;
+  pair[0] = x[e];
+  pair[1] = x[e + 1];
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(i16x2, pair), kOnesBf16x2, acc, false);
+}
+
+// P = 2^(s*c - kept), rounded to bf16, as the PV B operand; returns this
+// half-wave's sum of the ROUNDED values, so that O is normalised by exactly
+// the weights its P.V used (the output is then a convex combination of V
+// rows; normalising by the unrounded sum leaves a bias when a few large P
+// round the same way). Step t's operand: slots 0..3 <- block t/2,
+// j = 2(t%2); slots 4..7 <- j = 2(t%2)+1.
 template <int BN>
 __device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, float kept,
                                           bf16x8 (&pf)[BN / 16]) {
-  float ps = 0.0f;
 #pragma unroll
   for (int cb = 0; cb < BN / 32; ++cb)
 #pragma unroll
@@ -150,10 +180,17 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, f
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][4 * j + i], c, -kept));
-        ps += p;
         pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] = (__bf16)p;
       }
-  return ps;
+  float ps0 = 0.0f, ps1 = 0.0f;
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) {
+    ps0 = add_bf16_pair(ps0, pf[t], 0);
+    ps1 = add_bf16_pair(ps1, pf[t], 2);
+    ps0 = add_bf16_pair(ps0, pf[t], 4);
+    ps1 = add_bf16_pair(ps1, pf[t], 6);
+  }
+  return ps0 + ps1;
 }
 
 // O^T[d-block b] += V^T[b, step t] . P^T[step t] for one V tile.
@@ -321,8 +358,14 @@ void attn_fwd_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
 // workgroup after the next barrier.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0x0070); }
 // Workgroup barrier without the memory fence of __syncthreads (which would
-// also wait for loads that are meant to stay in flight across it).
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// also wait for loads that are meant to stay in flight across it). The
+// scheduling barriers stop the compiler from moving arithmetic across it,
+// which would blur the phases the barrier separates.
+__device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // K fragment for QK step u (u interleaves the 32-key blocks so consecutive
 // MFMAs feed independent accumulators): block u % (BN/32), dims chunk u / (BN/32).
@@ -340,38 +383,143 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vsm, int v_lane, int u) {
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The MFMA work of one phase: QK of a K tile into s and/or PV of a V tile
-// into acc, one MFMA of each per step, with the operands of step u+1
-// fetched from LDS while step u issues (scheduling barriers keep the
-// compiler from hoisting every fetch and running out of registers).
-template <int BN, bool kQK, bool kPV>
-__device__ __forceinline__ void mma_steps(const char* ksm, const char* vsm, int k_lane, int v_lane,
-                                          const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4]) {
-  constexpr int kSteps = BN / 4;  // = 8 * BN/32 QK MFMAs = 4 * BN/16 PV MFMAs
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 4
+#endif
+#ifndef ATTN_MMA_PRIO
+#define ATTN_MMA_PRIO 0
+#endif
+
+// LDS reads of the MFMA phase are issued as inline assembly with explicit
+// s_waitcnt lgkmcnt(N): the compiler's own counting gives up (waits for
+// everything) as soon as the loop also holds direct-to-LDS loads, which
+// would drain the operand ring every few MFMAs. LDS reads of one wave
+// complete in issue order, so N = the number of reads issued after the one
+// awaited. Each wait names the awaited registers as in/out operands, so no
+// use of them can move above it; volatile asm statements keep their order.
+template <int kOff>
+__device__ __forceinline__ u32x4 lds_b128(unsigned addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(kOff));
+  return r;
+}
+template <int kOff0, int kOff1>
+__device__ __forceinline__ void lds_tr_pair(unsigned addr, u32x2& lo, u32x2& hi) {
+  asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
+               : "=v"(lo), "=v"(hi) : "v"(addr), "i"(kOff0), "i"(kOff1));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x4& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait(u32x2& a, u32x2& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// Fragment f of an MFMA phase: f < kK is QK step f (K tile), then PV step
+// f - kK (V tile). A K fragment is one LDS read, a V fragment two.
+template <int BN>
+struct Frags {
+  static constexpr int kK = BN / 4;
+  static constexpr int kTotal = BN / 2;
+  static constexpr int ops(int f) { return f < kK ? 1 : 2; }
+  // reads issued after fragment f while it is awaited: fragments f+1 ..
+  // f+kPF-1 are in flight (the ring holds kPF fragments)
+  static constexpr int after(int f, int pf) {
+    int n = 0;
+    for (int g = f + 1; g < f + pf && g < kTotal; ++g) n += ops(g);
+    return n;
+  }
+};
+
+struct MmaRing {
+  u32x4 k[ATTN_PREFETCH];
+  u32x2 vlo[ATTN_PREFETCH], vhi[ATTN_PREFETCH];
+};
+
+template <int BN, int F>
+__device__ __forceinline__ void issue_frag(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
   constexpr int kCB = BN / 32;
-  if (kQK) {
-#pragma unroll
-    for (int cb = 0; cb < kCB; ++cb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[cb][i] = 0.0f;
+  constexpr int slot = F % ATTN_PREFETCH;
+  if constexpr (F < Frags<BN>::kK) {
+    ring.k[slot] = lds_b128<(F % kCB) * 8 * kKBlock + (F / kCB) * 128>(kaddr);
+  } else {
+    constexpr int u = F - Frags<BN>::kK;
+    constexpr int off = (u >> 2) * 4 * kVBlock + (u & 3) * 256;
+    lds_tr_pair<off, off + 2 * kVBlock>(vaddr, ring.vlo[slot], ring.vhi[slot]);
   }
-  bf16x8 ka = {}, va = {};
-  if (kQK) ka = k_frag<BN>(ksm, k_lane, 0);
-  if (kPV) va = v_frag(vsm, v_lane, 0);
-#pragma unroll
-  for (int u = 0; u < kSteps; ++u) {
-    bf16x8 kn = {}, vn = {};
-    if (u + 1 < kSteps) {
-      if (kQK) kn = k_frag<BN>(ksm, k_lane, u + 1);
-      if (kPV) vn = v_frag(vsm, v_lane, u + 1);
+}
+
+template <int BN, int F>
+__device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned vaddr,
+                                         const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
+                                         const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4]) {
+  constexpr int kCB = BN / 32;
+  constexpr int slot = F % ATTN_PREFETCH;
+  constexpr int N = Frags<BN>::after(F, ATTN_PREFETCH);
+  if constexpr (F < Frags<BN>::kK) {
+    lgkm_wait<N>(ring.k[slot]);
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
+    // the first MFMA of each score block starts from the constant 0
+    const f32x16 zero = {};
+    s[F % kCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[F / kCB], F < kCB ? zero : s[F % kCB],
+                                                         0, 0, 0);
+  } else {
+    constexpr int u = F - Frags<BN>::kK;
+    lgkm_wait<N>(ring.vlo[slot], ring.vhi[slot]);
+    const u32x4 a = __builtin_shufflevector(ring.vlo[slot], ring.vhi[slot], 0, 1, 2, 3);
+    // PV accumulates in place through a tied operand, which keeps each O
+    // accumulator in one register set (with the builtin the allocator moved
+    // all four between two sets every phase). Each accumulator is reused
+    // every fourth MFMA with exact dst/srcC overlap, which the hardware
+    // chains without wait states.
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                 : "+v"(acc[u & 3])
+                 : "v"(a), "v"(pf[u >> 2]));
+    if constexpr (F + 1 == Frags<BN>::kTotal) {
+      // The last MFMA's results are read by VALU code (rescale, epilogue)
+      // the compiler cannot see is dependent: give the 32x32 MFMA its
+      // write-back latency first.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]),
+                   "+v"(acc[3]));
     }
-    if (kQK) s[u % kCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[u / kCB], s[u % kCB], 0, 0, 0);
-    if (kPV) acc[u & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pf[u >> 2], acc[u & 3], 0, 0, 0);
-    ka = kn;
-    va = vn;
-    __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (F + ATTN_PREFETCH < Frags<BN>::kTotal) issue_frag<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
+  if constexpr (F + 1 < Frags<BN>::kTotal) mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc);
+}
+
+template <int BN, int F>
+__device__ __forceinline__ void issue_first(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
+  issue_frag<BN, F>(ring, kaddr, vaddr);
+  if constexpr (F + 1 < ATTN_PREFETCH) issue_first<BN, F + 1>(ring, kaddr, vaddr);
+}
+
+// The MFMA work of one phase: QK of a K tile into s, then PV of a V tile
+// into acc, with the LDS operands ATTN_PREFETCH fragments ahead of use.
+template <int BN>
+__device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
+                                          const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
+                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha) {
+  // O is rescaled here, in the MFMA phase, by the factor the softmax phase
+  // chose (1 for rows that kept their base): keeping every VALU write of O
+  // next to the MFMAs that use it lets O stay in one set of registers.
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+  const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
+  const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
+  MmaRing ring;
+  issue_first<BN, 0>(ring, kaddr, vaddr);
+  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc);
+}
+
+// QK of one K tile only (first phase), same scheme with plain builtins.
+template <int BN>
+__device__ __forceinline__ void qk_only(const char* ksm, int k_lane, const bf16x8 (&qf)[8],
+                                        f32x16 (&s)[BN / 32]) {
+  qk_tile<BN>(ksm, k_lane, qf, s);
 }
 
 // MFMA phase i >= 1 of the eight-wave kernel: PV(i-1) and QK(i), then
@@ -381,27 +529,34 @@ __device__ __forceinline__ void mma_steps(const char* ksm, const char* vsm, int 
 template <int BN>
 __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, int k_lane,
                                            int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                           const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4]) {
-  mma_steps<BN, true, true>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc);
+                                           const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
+                                           float alpha) {
+#if ATTN_MMA_PRIO
+  __builtin_amdgcn_s_setprio(ATTN_MMA_PRIO);
+#endif
+  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha);
+#if ATTN_MMA_PRIO
+  __builtin_amdgcn_s_setprio(0);
+#endif
   wait_mem();
   barrier();
 }
 
 // Softmax phase i: group B first issues the loads of K(i+2) (into the
-// buffer K(i) left) and V(i+1); then the base update, which rescales O
-// (already holding PV(i-1)) if needed, and P(i).
+// buffer K(i) left) and V(i+1); then the base update, whose factor for O
+// (already holding PV(i-1)) the next MFMA phase applies, and P(i).
 template <int BN>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
                                            char* vnext, float c, const f32x16 (&s)[BN / 32],
-                                           bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float& kept,
+                                           bf16x8 (&pf)[BN / 16], float& alpha, float& kept,
                                            float& lsum) {
   constexpr int kTileBytes = BN * kD * 2;
   if (group == 1) {
     if (i + 2 < ntiles) load_tile<BN, kKBlock>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
     if (i + 1 < ntiles) load_tile<BN, kVBlock>(vg + int64_t(i + 1) * kTileBytes, vfill, vnext, wave);
   }
-  update_base(tile_max<BN>(s), c, kept, lsum, acc);
+  alpha = base_update_alpha(tile_max<BN>(s), c, kept, lsum);
   lsum += exp_tile<BN>(s, c, kept, pf);
   barrier();
 }
@@ -501,19 +656,21 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   if (group == 1) barrier();  // phase shift: B starts one interval later
 
   // M(0) is QK(0) alone; after it every MFMA phase i holds PV(i-1) and
-  // QK(i). Buffers alternate with i; the loop is unrolled by two so that
-  // each half names its buffers statically.
-  mma_steps<BN, true, false>(kb0, vb0, k_lane, v_lane, qf, s, pf, acc);
+  // QK(i). K(i) and V(i) live in buffer i % 2. One loop body for all
+  // phases keeps every accumulator in a single set of registers (an
+  // unrolled pair of bodies made the compiler shuttle them between two).
+  qk_only<BN>(kb0, k_lane, qf, s);
   wait_mem();
   barrier();
-  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, acc, kept, lsum);
-  for (int i = 1;; i += 2) {
-    pp_m_phase<BN>(kb1, vb0, k_lane, v_lane, qf, s, pf, acc);
+  float alpha;
+  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, alpha, kept, lsum);
+  for (int i = 1;; ++i) {
+    const bool odd = i & 1;
+    char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
+    char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
+    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha);
     if (i == ntiles) break;
-    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, kb1, vb0, c, s, pf, acc, kept, lsum);
-    pp_m_phase<BN>(kb0, vb1, k_lane, v_lane, qf, s, pf, acc);
-    if (i + 1 == ntiles) break;
-    pp_v_phase<BN>(i + 1, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, acc, kept,
+    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, v_other, c, s, pf, alpha, kept,
                    lsum);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
@@ -537,7 +694,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 }  // namespace
 
 #ifndef ATTN_PP_BN
-#define ATTN_PP_BN 64
+#define ATTN_PP_BN 128
 #endif
 #ifndef ATTN_PP_MIN_WGS
 #define ATTN_PP_MIN_WGS 512

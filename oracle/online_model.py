@@ -31,6 +31,12 @@ article's claim that skipping a rescale loses no information. With
 P.V product while the row sum keeps the unrounded P (Chapter 1, section B,
 P written as bf16 after adding to the row sum); that variant estimates the
 error a kernel with bf16 P has, it is not the reference result.
+``rowsum_of_rounded=True`` (with ``p_to_bf16``) instead sums the same
+rounded P that enters P.V, so O is divided by exactly the total weight its
+accumulator received and stays a convex combination of V rows. Where a
+few large P dominate a row and round the same way, the unrounded sum
+leaves a bias of up to 2^-9 relative on the whole row; summing the rounded
+values removes it.
 """
 from __future__ import annotations
 
@@ -69,7 +75,8 @@ def _bf16_rne(x: torch.Tensor) -> torch.Tensor:
 
 def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
                 block_n: int, thresh_log2: float = REBASE_THRESH_LOG2,
-                p_to_bf16: bool = False, stats: dict | None = None):
+                p_to_bf16: bool = False, stats: dict | None = None,
+                rowsum_of_rounded: bool = False):
     """One query tile q [M, D] against k, v [S, D] (float64). Returns (O [M, D], lse [M])."""
     M = q.shape[0]
     S = k.shape[0]
@@ -96,8 +103,8 @@ def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
         p = _ftz(torch.exp2(s_raw * c - kept[:, None]))  # unnormalised P against the kept base
         if stats is not None:
             stats["max_p"] = max(stats.get("max_p", 0.0), float(p.max()))
-        rowsum = rowsum + p.sum(dim=1)                   # row sum from unrounded P
         pv = _bf16_rne(p) if p_to_bf16 else p
+        rowsum = rowsum + (pv if rowsum_of_rounded else p).sum(dim=1)
         acc = acc + pv @ vt
     if stats is not None:
         stats["rebases"] = stats.get("rebases", 0) + rebases
@@ -109,7 +116,8 @@ def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
 def online_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: float,
                      block_m: int = 128, block_n: int = 128,
                      thresh_log2: float = REBASE_THRESH_LOG2, p_to_bf16: bool = False,
-                     stats: dict | None = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     stats: dict | None = None,
+                     rowsum_of_rounded: bool = False) -> Tuple[torch.Tensor, torch.Tensor]:
     """Online-softmax attention over [B, H, S, D] inputs; returns float64 (O, lse)."""
     if scale <= 0:
         raise ValueError("the max of raw scores commutes with the scale only for scale > 0")
@@ -124,5 +132,5 @@ def online_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: f
             for i0 in range(0, S, block_m):
                 qd = q[b, h, i0:i0 + block_m].to(torch.float64)
                 o[b, h, i0:i0 + block_m], lse[b, h, i0:i0 + block_m] = online_tile(
-                    qd, kd, vd, sigma, block_n, thresh_log2, p_to_bf16, stats)
+                    qd, kd, vd, sigma, block_n, thresh_log2, p_to_bf16, stats, rowsum_of_rounded)
     return o, lse

@@ -2,10 +2,10 @@
 
 Bar: O max-abs error <= 2e-2 and mean-abs error <= 2e-3 against the
 unrounded fp64 O; LSE relative error <= 1e-3 (denominator max(|lse|, 1)).
-Small shapes and the two smaller workloads are compared element by element
-over the whole output; the 4K/8K/16K workloads run at full size in the
-benchmark's launch configuration and are compared on sampled rows, plus
-properties that hold at any size.
+Small shapes and all five workloads, at full size and in the launch
+configuration the benchmark times, are compared element by element over the
+whole output (the fp64 oracle finishes the 16K workload in seconds on a
+multi-core host), plus properties that hold at any size.
 """
 import math
 import sys
@@ -83,50 +83,38 @@ def test_small_shapes_full(daf, B, H, S, seed, std, vd, frac, variant):
     _assert_parity(o, lse, o_ref, lse_ref, f"small {B}x{H}x{S} v{variant}")
 
 
+_REF = {}
+
+
+def _reference(w):
+    """Inputs and oracle result of a workload, kept for the next variant."""
+    if w.name not in _REF:
+        _REF.clear()
+        q, k, v = make_inputs(w)
+        _REF[w.name] = (q, k, v) + oracle.attention(q, k, v, w.scale)
+    return _REF[w.name]
+
+
 @pytest.mark.parametrize("variant", [0] + VARIANTS)
-@pytest.mark.parametrize("name", ["s256", "s1k"])
+@pytest.mark.parametrize("name", [w.name for w in workloads.WORKLOADS])
 def test_workload_full(daf, name, variant):
+    """Every workload at full size, compared element by element over the
+    whole output. Variant 0 is the launch configuration the benchmark times
+    (the library's own pick); 1 and 2 force each layout."""
     w = workloads.get(name)
-    _say(f"case workload {w.describe()} variant={variant}")
-    q, k, v = make_inputs(w)
+    chosen = daf.pick(w.B, w.H, w.S) if variant == 0 else variant
+    _say(f"case workload {w.describe()} variant={variant} (runs {chosen})")
+    q, k, v, o_ref, lse_ref = _reference(w)
     o, lse = _run(daf, q, k, v, w.scale, variant=variant)
-    o_ref, lse_ref = oracle.attention(q, k, v, w.scale)
-    _assert_parity(o, lse, o_ref, lse_ref, f"{name} v{variant}")
-
-
-def _picks(w, n_random=160, seed=0):
-    gen = torch.Generator().manual_seed(seed)
-    picks = set()
-    for b in range(w.B):
-        for h in range(w.H):
-            for r in (0, 127, 128, w.S // 2, w.S - 129, w.S - 1):
-                picks.add((b, h, r))
-    bs = torch.randint(0, w.B, (n_random,), generator=gen)
-    hs = torch.randint(0, w.H, (n_random,), generator=gen)
-    rs = torch.randint(0, w.S, (n_random,), generator=gen)
-    for b, h, r in zip(bs.tolist(), hs.tolist(), rs.tolist()):
-        picks.add((b, h, r))
-    return sorted(picks)
-
-
-@pytest.mark.parametrize("name", ["s4k", "s8k_peaked", "s16k_outliers"])
-def test_workload_sampled(daf, name):
-    """Full size, in the launch configuration the benchmark times (attn_fwd's own pick)."""
-    w = workloads.get(name)
-    _say(f"case workload {w.describe()} (full size, sampled rows, variant {daf.pick(w.B, w.H, w.S)})")
-    q, k, v = make_inputs(w)
-    o, lse = _run(daf, q, k, v, w.scale)
-    # properties over the whole output
+    # properties over the whole output: finite, inside the hull of V, lse
+    # at least the largest scaled score (here > 0)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    of = o.float()
     vmin = v.float().amin(dim=2, keepdim=True)
     vmax = v.float().amax(dim=2, keepdim=True)
-    of = o.float()
     assert (of >= vmin - O_MAX).all() and (of <= vmax + O_MAX).all(), "O outside the hull of V"
     assert (lse > 0).all()
-    picks = _picks(w)
-    o_ref, lse_ref = oracle.attention_rows(q, k, v, w.scale, picks)
-    idx = tuple(torch.tensor(x) for x in zip(*picks))
-    _assert_parity(o[idx], lse[idx], o_ref, lse_ref, f"{name} ({len(picks)} sampled rows)")
+    _assert_parity(o, lse, o_ref, lse_ref, f"{name} v{variant}")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -139,13 +127,15 @@ def test_deterministic(daf, variant):
 
 
 def test_variants_agree(daf):
-    """Both layouts run the same per-row arithmetic in the same order, so
-    they agree bit for bit."""
+    """The two layouts use different K/V tile lengths, so their lazy rebases
+    fall on different keys and the results differ by rounding only."""
     _say("case variants agree")
     q, k, v = make_random(1, 3, 640, 128, seed=28, qk_std=2.0)
     o1, l1 = _run(daf, q, k, v, variant=1)
     o2, l2 = _run(daf, q, k, v, variant=2)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    d = (o1.double() - o2.double()).abs()
+    assert d.max().item() <= O_MAX and d.mean().item() <= O_MEAN
+    assert ((l1.double() - l2.double()).abs() / l2.double().abs().clamp_min(1.0)).max().item() <= LSE_REL
 
 
 def test_side_stream_and_full_overwrite(daf):

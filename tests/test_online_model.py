@@ -134,3 +134,35 @@ def test_nonpositive_scale_rejected():
     q, k, v = make_random(1, 1, 128, 128, seed=3006)
     with pytest.raises(ValueError):
         online_model.online_attention(q, k, v, -1.0)
+
+
+def test_rounded_rowsum_keeps_constant_v_exact():
+    """Softmax weights sum to one, so O of a constant V is that constant.
+    Dividing by the sum of the same bf16 P that entered P.V keeps this to
+    fp64 rounding; dividing by the unrounded sum does not (it is off by the
+    rounding of P, up to 2^-9 relative)."""
+    q, k, _ = make_random(1, 2, 384, 128, seed=3007, qk_std=2.0)
+    v = torch.full_like(q, 0.75)
+    o, _ = online_model.online_attention(q, k, v, DEFAULT_SCALE, p_to_bf16=True,
+                                         rowsum_of_rounded=True)
+    assert (o - 0.75).abs().max().item() < 1e-14
+    o_unr, _ = online_model.online_attention(q, k, v, DEFAULT_SCALE, p_to_bf16=True)
+    off = (o_unr - 0.75).abs().max().item()
+    assert 1e-6 < off <= 0.75 * 2.0 ** -8
+
+
+def test_rounded_rowsum_error_on_outlier_recipe():
+    """The 1%-outlier-key recipe with the rounded-P row sum stays inside the
+    O tolerance with margin. The LSE taken from that sum differs from the
+    exact one by at most -ln(1 - 2^-8) in absolute terms (each P is off by
+    at most 2^-8 relative), which is within the 1e-3 relative bar wherever
+    |lse| >= 3.9."""
+    q, k, v = make_random(1, 2, 1024, 128, seed=3008, outlier_frac=0.01)
+    o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, p_to_bf16=True,
+                                           rowsum_of_rounded=True)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    err = (o - o_ref).abs()
+    assert err.max().item() < 2e-2 / 2 and err.mean().item() < 2e-3 / 2
+    assert (lse - lse_ref).abs().max().item() <= -math.log1p(-2.0 ** -8)
+    rel = ((lse - lse_ref).abs() / lse_ref.abs().clamp_min(1.0)).max().item()
+    assert rel < 1e-3 / 2
