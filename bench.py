@@ -111,11 +111,11 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=HEADLINE, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-also", action="store_true", help="skip the other sequence lengths")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU-baseline sample")
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
                          "reference reading for the HBM byte counters) and exit")
