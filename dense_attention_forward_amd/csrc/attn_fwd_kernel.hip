@@ -500,14 +500,18 @@ __device__ __forceinline__ void issue_first(MmaRing& ring, unsigned kaddr, unsig
 template <int BN>
 __device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                           const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha) {
+                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha,
+                                          bool rescale) {
   // O is rescaled here, in the MFMA phase, by the factor the softmax phase
-  // chose (1 for rows that kept their base): keeping every VALU write of O
+  // chose (1 for rows that kept their base), and only when some row of the
+  // wave rebased (`rescale` is wave-uniform): keeping every VALU write of O
   // next to the MFMAs that use it lets O stay in one set of registers.
+  if (rescale) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+      for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+  }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing ring;
@@ -530,11 +534,11 @@ template <int BN>
 __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, int k_lane,
                                            int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                            const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                           float alpha) {
+                                           float alpha, bool rescale) {
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(ATTN_MMA_PRIO);
 #endif
-  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha);
+  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(0);
 #endif
@@ -549,14 +553,15 @@ template <int BN>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
                                            char* vnext, float c, const f32x16 (&s)[BN / 32],
-                                           bf16x8 (&pf)[BN / 16], float& alpha, float& kept,
-                                           float& lsum) {
+                                           bf16x8 (&pf)[BN / 16], float& alpha, bool& rescale,
+                                           float& kept, float& lsum) {
   constexpr int kTileBytes = BN * kD * 2;
   if (group == 1) {
     if (i + 2 < ntiles) load_tile<BN, kKBlock>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
     if (i + 1 < ntiles) load_tile<BN, kVBlock>(vg + int64_t(i + 1) * kTileBytes, vfill, vnext, wave);
   }
   alpha = base_update_alpha(tile_max<BN>(s), c, kept, lsum);
+  rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
   lsum += exp_tile<BN>(s, c, kept, pf);
   barrier();
 }
@@ -663,15 +668,17 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   wait_mem();
   barrier();
   float alpha;
-  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, alpha, kept, lsum);
+  bool rescale;
+  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, alpha, rescale, kept,
+                 lsum);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
     char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
-    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha);
+    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
     if (i == ntiles) break;
-    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, v_other, c, s, pf, alpha, kept,
-                   lsum);
+    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, v_other, c, s, pf, alpha, rescale,
+                   kept, lsum);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
 
