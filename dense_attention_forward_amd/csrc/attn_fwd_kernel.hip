@@ -47,6 +47,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -98,11 +99,10 @@ __device__ __forceinline__ int v_fill_offset(int l) {
 // Base update without touching O: returns the factor O must be multiplied
 // by before the next P.V (1 for rows that keep their base; exactly 1.0, so
 // multiplying by it changes nothing).
-__device__ __forceinline__ float base_update_alpha(float raw_max, float c, float& kept, float& lsum) {
+__device__ __forceinline__ float base_update_alpha(float raw_max, float c, float& kept) {
   const float cand = fmaxf(kept, raw_max * c);
   const bool need = (cand - kept) >= kRebaseLog2;
   const float alpha = need ? __builtin_amdgcn_exp2f(kept - cand) : 1.0f;
-  lsum *= alpha;
   kept = need ? cand : kept;
   return alpha;
 }
@@ -191,6 +191,31 @@ __device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, f
     ps1 = add_bf16_pair(ps1, pf[t], 6);
   }
   return ps0 + ps1;
+}
+
+// P = 2^(s*c - kept), rounded to bf16, as the PV B operand (layout as in
+// exp_tile), without a row sum.
+template <int BN>
+__device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, float kept,
+                                           bf16x8 (&pf)[BN / 16]) {
+#pragma unroll
+  for (int cb = 0; cb < BN / 32; ++cb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][4 * j + i], c, -kept));
+        pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] = (__bf16)p;
+      }
+}
+
+// The other half-wave's value of x (lane l <-> lane l ^ 32), through
+// v_permlane32_swap, which exchanges the upper half of its first operand
+// with the lower half of its second: with x in both, lanes 0-31 find the
+// partner's value in the second result and lanes 32-63 in the first.
+__device__ __forceinline__ float max_with_other_half(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
 // O^T[d-block b] += V^T[b, step t] . P^T[step t] for one V tile.
@@ -357,6 +382,8 @@ void attn_fwd_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
 // (s_waitcnt vmcnt(0) lgkmcnt(0)); the data is then visible to the whole
 // workgroup after the next barrier.
 __device__ __forceinline__ void wait_mem() { __builtin_amdgcn_s_waitcnt(0x0070); }
+// s_waitcnt vmcnt(0) alone: this wave's loads have landed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Workgroup barrier without the memory fence of __syncthreads (which would
 // also wait for loads that are meant to stay in flight across it). The
 // scheduling barriers stop the compiler from moving arithmetic across it,
@@ -388,6 +415,9 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vsm, int v_lane, int u) {
 #endif
 #ifndef ATTN_MMA_PRIO
 #define ATTN_MMA_PRIO 0
+#endif
+#ifndef ATTN_STEP_FENCE
+#define ATTN_STEP_FENCE 1
 #endif
 
 // LDS reads of the MFMA phase are issued as inline assembly with explicit
@@ -454,7 +484,8 @@ __device__ __forceinline__ void issue_frag(MmaRing& ring, unsigned kaddr, unsign
 template <int BN, int F>
 __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned vaddr,
                                          const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                         const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4]) {
+                                         const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
+                                         f32x4& lacc, const bf16x8& sel, float& mx) {
   constexpr int kCB = BN / 32;
   constexpr int slot = F % ATTN_PREFETCH;
   constexpr int N = Frags<BN>::after(F, ATTN_PREFETCH);
@@ -477,16 +508,33 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
                  : "+v"(acc[u & 3])
                  : "v"(a), "v"(pf[u >> 2]));
+    // After the fourth MFMA of key step u/4, the same P fragment meets the
+    // selector operand in a 16x16x32 MFMA that adds the step's 16 keys of
+    // both half-waves into the row sum (lane l, register 0 holds the sum of
+    // query l % 32). The sum thus takes exactly the rounded P the PV used,
+    // on the matrix pipe instead of the vector ALU.
+    if constexpr ((u & 3) == 3)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(lacc) : "v"(sel), "v"(pf[u >> 2]));
+    // Beside each PV MFMA, two of the new scores (the QK MFMAs above have
+    // drained by now) join the raw row max: BN/4 PV steps, BN/2 scores.
+    constexpr int j0 = 2 * u;
+    mx = __builtin_elementwise_maximum(
+        mx, __builtin_elementwise_maximum(s[j0 / 16][j0 % 16], s[j0 / 16][j0 % 16 + 1]));
     if constexpr (F + 1 == Frags<BN>::kTotal) {
-      // The last MFMA's results are read by VALU code (rescale, epilogue)
+      // The last MFMAs' results are read by VALU code (rescale, epilogue)
       // the compiler cannot see is dependent: give the 32x32 MFMA its
       // write-back latency first.
       asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]),
-                   "+v"(acc[3]));
+                   "+v"(acc[3]), "+v"(lacc));
     }
   }
   if constexpr (F + ATTN_PREFETCH < Frags<BN>::kTotal) issue_frag<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
-  if constexpr (F + 1 < Frags<BN>::kTotal) mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc);
+#if ATTN_STEP_FENCE
+  // Keep each step's VALU work beside its MFMA.
+  __builtin_amdgcn_sched_barrier(0);
+#endif
+  if constexpr (F + 1 < Frags<BN>::kTotal)
+    mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel, mx);
 }
 
 template <int BN, int F>
@@ -501,7 +549,7 @@ template <int BN>
 __device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                           const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                           const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha,
-                                          bool rescale) {
+                                          bool rescale, f32x4& lacc, const bf16x8& sel, float& mx) {
   // O is rescaled here, in the MFMA phase, by the factor the softmax phase
   // chose (1 for rows that kept their base), and only when some row of the
   // wave rebased (`rescale` is wave-uniform): keeping every VALU write of O
@@ -511,12 +559,14 @@ __device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int 
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
+    lacc[0] *= alpha;
   }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing ring;
   issue_first<BN, 0>(ring, kaddr, vaddr);
-  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc);
+  mx = -FLT_MAX;
+  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel, mx);
 }
 
 // QK of one K tile only (first phase), same scheme with plain builtins.
@@ -534,14 +584,17 @@ template <int BN>
 __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, int k_lane,
                                            int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                            const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                           float alpha, bool rescale) {
+                                           float alpha, bool rescale, f32x4& lacc, const bf16x8& sel,
+                                           float& raw_max) {
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(ATTN_MMA_PRIO);
 #endif
-  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
+  float mx;
+  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel, mx);
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(0);
 #endif
+  raw_max = max_with_other_half(mx);
   wait_mem();
   barrier();
 }
@@ -552,17 +605,29 @@ __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, 
 template <int BN>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
-                                           char* vnext, float c, const f32x16 (&s)[BN / 32],
-                                           bf16x8 (&pf)[BN / 16], float& alpha, bool& rescale,
-                                           float& kept, float& lsum) {
+                                           char* vcur, float c, const f32x16 (&s)[BN / 32],
+                                           float raw_max, bf16x8 (&pf)[BN / 16], float& alpha,
+                                           bool& rescale, float& kept) {
   constexpr int kTileBytes = BN * kD * 2;
+  // The two groups split the loads so that each phase pair moves one tile:
+  // group B fetches K(i+2) into the buffer K(i) left, group A fetches V(i)
+  // into the buffer V(i-2) left (both buffers' last readers finished in the
+  // previous interval). A waits for its loads at the end of this phase;
+  // B's are awaited at the end of its next MFMA phase.
   if (group == 1) {
     if (i + 2 < ntiles) load_tile<BN, kKBlock>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
-    if (i + 1 < ntiles) load_tile<BN, kVBlock>(vg + int64_t(i + 1) * kTileBytes, vfill, vnext, wave);
+  } else if (i >= 1) {
+    load_tile<BN, kVBlock>(vg + int64_t(i) * kTileBytes, vfill, vcur, wave);
   }
-  alpha = base_update_alpha(tile_max<BN>(s), c, kept, lsum);
+  alpha = base_update_alpha(raw_max, c, kept);
   rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-  lsum += exp_tile<BN>(s, c, kept, pf);
+  exp_tile_p<BN>(s, c, kept, pf);
+  // P must be complete here, not computed after the barrier where it is
+  // first used: the overlap of this phase with the other group's MFMAs
+  // depends on it.
+#pragma unroll
+  for (int t = 0; t < BN / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  if (group == 0) wait_vmem();
   barrier();
 }
 
@@ -575,10 +640,15 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 //
 // Group A runs M(0) V(0) M(1) V(1) ... M(n); group B starts one barrier
 // later, so interval 2i+1 holds A's V(i) and B's M(i), interval 2i+2 A's
-// M(i+1) and B's V(i). K(i) and V(i) live in buffer i%2; K(i+2) and V(i+1)
-// are loaded by group B at the start of its V(i) (their buffers' last
-// readers finished by then) and waited for at the end of its M(i+1), one
-// barrier before group A first reads them.
+// M(i+1) and B's V(i). K(i) and V(i) live in buffer i%2. K(i+2) is loaded
+// by group B at the start of its V(i) and awaited at the end of its M(i+1);
+// V(i) is loaded by group A at the start of its V(i) and awaited at its
+// end. Each interval thus moves one tile through the load path (issuing
+// both in one phase stalled that phase for the whole transfer).
+//
+// The MFMA phase also takes the raw row max of its new scores and the row
+// sum of the P it consumes (on the matrix pipe), so the softmax phase is
+// left with the base update and the exponentials.
 template <int BN>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
@@ -649,7 +719,22 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
   float kept = -FLT_MAX;
-  float lsum = 0.0f;
+  // Row sum: register 0 of lacc, accumulated on the matrix pipe by
+  // v_mfma_f32_16x16x32_bf16 with the selector `sel` as A operand. The
+  // B operand is a PV fragment: lane l holds 8 keys of query l % 32, in the
+  // 16x16x32 layout column l % 16 and k-group l / 16 (groups 0 and 2 belong
+  // to query c = l % 16, groups 1 and 3 to query c + 16). Selector row r
+  // has ones on the groups of query c (r = 0, 8) or c + 16 (r = 4, 12) and
+  // zeros elsewhere; output row 4 * (l / 16) of column l % 16 then lands in
+  // lane l, register 0, as the sum for query l % 32. Registers 1-3 stay 0.
+  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};
+  bf16x8 sel;
+  {
+    const int r = lane & 15, g = lane >> 4;
+    const bool on = ((r == 0 || r == 8) && !(g & 1)) || ((r == 4 || r == 12) && (g & 1));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(on ? 1.0f : 0.0f);
+  }
   f32x16 s[BN / 32];
   bf16x8 pf[BN / 16];
 #pragma unroll
@@ -665,25 +750,26 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // phases keeps every accumulator in a single set of registers (an
   // unrolled pair of bodies made the compiler shuttle them between two).
   qk_only<BN>(kb0, k_lane, qf, s);
+  float raw_max = tile_max<BN>(s);
   wait_mem();
   barrier();
   float alpha;
   bool rescale;
-  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb1, c, s, pf, alpha, rescale, kept,
-                 lsum);
+  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, raw_max, pf, alpha,
+                 rescale, kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
     char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
-    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
+    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel, raw_max);
     if (i == ntiles) break;
-    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, v_other, c, s, pf, alpha, rescale,
-                   kept, lsum);
+    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, raw_max, pf, alpha,
+                   rescale, kept);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
 
   if (!valid) return;
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = lacc[0];
   const float inv = 1.0f / ltot;
   __bf16* orow = o + head + int64_t(qrow) * kD;
 #pragma unroll
