@@ -218,6 +218,20 @@ __device__ __forceinline__ float max_with_other_half(float x) {
   return __builtin_elementwise_maximum(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+// Raw row max of a score tile over both half-waves, with v_maximum3 (fmaxf's
+// NaN rule would add a quieting v_max per MFMA result; inputs are finite
+// by contract) and the half-wave exchange on v_permlane32_swap.
+template <int BN>
+__device__ __forceinline__ float tile_max_swap(const f32x16 (&s)[BN / 32]) {
+  float mx = -FLT_MAX;
+#pragma unroll
+  for (int cb = 0; cb < BN / 32; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2)
+      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[cb][i], s[cb][i + 1]));
+  return max_with_other_half(mx);
+}
+
 // O^T[d-block b] += V^T[b, step t] . P^T[step t] for one V tile.
 template <int BN>
 __device__ __forceinline__ void pv_tile(const char* vsm, int v_lane, const bf16x8 (&pf)[BN / 16],
@@ -485,7 +499,7 @@ template <int BN, int F>
 __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned vaddr,
                                          const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                         f32x4& lacc, const bf16x8& sel, float& mx) {
+                                         f32x4& lacc, const bf16x8& sel) {
   constexpr int kCB = BN / 32;
   constexpr int slot = F % ATTN_PREFETCH;
   constexpr int N = Frags<BN>::after(F, ATTN_PREFETCH);
@@ -515,11 +529,6 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
     // on the matrix pipe instead of the vector ALU.
     if constexpr ((u & 3) == 3)
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(lacc) : "v"(sel), "v"(pf[u >> 2]));
-    // Beside each PV MFMA, two of the new scores (the QK MFMAs above have
-    // drained by now) join the raw row max: BN/4 PV steps, BN/2 scores.
-    constexpr int j0 = 2 * u;
-    mx = __builtin_elementwise_maximum(
-        mx, __builtin_elementwise_maximum(s[j0 / 16][j0 % 16], s[j0 / 16][j0 % 16 + 1]));
     if constexpr (F + 1 == Frags<BN>::kTotal) {
       // The last MFMAs' results are read by VALU code (rescale, epilogue)
       // the compiler cannot see is dependent: give the 32x32 MFMA its
@@ -534,7 +543,7 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
   __builtin_amdgcn_sched_barrier(0);
 #endif
   if constexpr (F + 1 < Frags<BN>::kTotal)
-    mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel, mx);
+    mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel);
 }
 
 template <int BN, int F>
@@ -549,7 +558,7 @@ template <int BN>
 __device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                           const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                           const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha,
-                                          bool rescale, f32x4& lacc, const bf16x8& sel, float& mx) {
+                                          bool rescale, f32x4& lacc, const bf16x8& sel) {
   // O is rescaled here, in the MFMA phase, by the factor the softmax phase
   // chose (1 for rows that kept their base), and only when some row of the
   // wave rebased (`rescale` is wave-uniform): keeping every VALU write of O
@@ -565,8 +574,7 @@ __device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int 
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing ring;
   issue_first<BN, 0>(ring, kaddr, vaddr);
-  mx = -FLT_MAX;
-  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel, mx);
+  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel);
 }
 
 // QK of one K tile only (first phase), same scheme with plain builtins.
@@ -584,17 +592,14 @@ template <int BN>
 __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, int k_lane,
                                            int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                            const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                           float alpha, bool rescale, f32x4& lacc, const bf16x8& sel,
-                                           float& raw_max) {
+                                           float alpha, bool rescale, f32x4& lacc, const bf16x8& sel) {
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(ATTN_MMA_PRIO);
 #endif
-  float mx;
-  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel, mx);
+  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
 #if ATTN_MMA_PRIO
   __builtin_amdgcn_s_setprio(0);
 #endif
-  raw_max = max_with_other_half(mx);
   wait_mem();
   barrier();
 }
@@ -606,8 +611,8 @@ template <int BN>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
                                            char* vcur, float c, const f32x16 (&s)[BN / 32],
-                                           float raw_max, bf16x8 (&pf)[BN / 16], float& alpha,
-                                           bool& rescale, float& kept) {
+                                           bf16x8 (&pf)[BN / 16], float& alpha, bool& rescale,
+                                           float& kept) {
   constexpr int kTileBytes = BN * kD * 2;
   // The two groups split the loads so that each phase pair moves one tile:
   // group B fetches K(i+2) into the buffer K(i) left, group A fetches V(i)
@@ -619,7 +624,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
   } else if (i >= 1) {
     load_tile<BN, kVBlock>(vg + int64_t(i) * kTileBytes, vfill, vcur, wave);
   }
-  alpha = base_update_alpha(raw_max, c, kept);
+  alpha = base_update_alpha(tile_max_swap<BN>(s), c, kept);
   rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
   exp_tile_p<BN>(s, c, kept, pf);
   // P must be complete here, not computed after the barrier where it is
@@ -646,9 +651,9 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 // end. Each interval thus moves one tile through the load path (issuing
 // both in one phase stalled that phase for the whole transfer).
 //
-// The MFMA phase also takes the raw row max of its new scores and the row
-// sum of the P it consumes (on the matrix pipe), so the softmax phase is
-// left with the base update and the exponentials.
+// The MFMA phase also takes the row sum of the P it consumes, on the matrix
+// pipe; the softmax phase keeps the row max, the base update and the
+// exponentials.
 template <int BN>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
@@ -750,20 +755,19 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // phases keeps every accumulator in a single set of registers (an
   // unrolled pair of bodies made the compiler shuttle them between two).
   qk_only<BN>(kb0, k_lane, qf, s);
-  float raw_max = tile_max<BN>(s);
   wait_mem();
   barrier();
   float alpha;
   bool rescale;
-  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, raw_max, pf, alpha,
-                 rescale, kept);
+  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha, rescale,
+                 kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
     char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
-    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel, raw_max);
+    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
     if (i == ntiles) break;
-    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, raw_max, pf, alpha,
+    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                    rescale, kept);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
