@@ -454,11 +454,13 @@ __device__ __forceinline__ void lds_tr_pair(unsigned addr, u32x2& lo, u32x2& hi)
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x4& r) {
-  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+  asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(N));
+  __builtin_amdgcn_sched_barrier(0);
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait(u32x2& a, u32x2& b) {
-  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+  asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(N));
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Fragment f of an MFMA phase: f < kK is QK step f (K tile), then PV step
