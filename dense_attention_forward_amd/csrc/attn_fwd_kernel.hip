@@ -439,8 +439,10 @@ __device__ __forceinline__ bf16x8 v_frag(const char* vsm, int v_lane, int u) {
 // everything) as soon as the loop also holds direct-to-LDS loads, which
 // would drain the operand ring every few MFMAs. LDS reads of one wave
 // complete in issue order, so N = the number of reads issued after the one
-// awaited. Each wait names the awaited registers as in/out operands, so no
-// use of them can move above it; volatile asm statements keep their order.
+// awaited. A scheduling barrier after each wait keeps every use of the
+// awaited registers below it (naming them as in/out operands of the wait
+// did too, but made the hazard recognizer pad each MFMA with an s_nop);
+// volatile asm statements keep their order among themselves.
 template <int kOff>
 __device__ __forceinline__ u32x4 lds_b128(unsigned addr) {
   u32x4 r;
@@ -453,12 +455,7 @@ __device__ __forceinline__ void lds_tr_pair(unsigned addr, u32x2& lo, u32x2& hi)
                : "=v"(lo), "=v"(hi) : "v"(addr), "i"(kOff0), "i"(kOff1));
 }
 template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x4& r) {
-  asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(N));
-  __builtin_amdgcn_sched_barrier(0);
-}
-template <int N>
-__device__ __forceinline__ void lgkm_wait(u32x2& a, u32x2& b) {
+__device__ __forceinline__ void lgkm_wait() {
   asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(N));
   __builtin_amdgcn_sched_barrier(0);
 }
@@ -506,7 +503,7 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
   constexpr int slot = F % ATTN_PREFETCH;
   constexpr int N = Frags<BN>::after(F, ATTN_PREFETCH);
   if constexpr (F < Frags<BN>::kK) {
-    lgkm_wait<N>(ring.k[slot]);
+    lgkm_wait<N>();
     const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
     // the first MFMA of each score block starts from the constant 0
     const f32x16 zero = {};
@@ -514,7 +511,7 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
                                                          0, 0, 0);
   } else {
     constexpr int u = F - Frags<BN>::kK;
-    lgkm_wait<N>(ring.vlo[slot], ring.vhi[slot]);
+    lgkm_wait<N>();
     const u32x4 a = __builtin_shufflevector(ring.vlo[slot], ring.vhi[slot], 0, 1, 2, 3);
     // PV accumulates in place through a tied operand, which keeps each O
     // accumulator in one register set (with the builtin the allocator moved
