@@ -408,30 +408,8 @@ __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// K fragment for QK step u (u interleaves the 32-key blocks so consecutive
-// MFMAs feed independent accumulators): block u % (BN/32), dims chunk u / (BN/32).
-template <int BN>
-__device__ __forceinline__ bf16x8 k_frag(const char* ksm, int k_lane, int u) {
-  constexpr int kCB = BN / 32;
-  return *reinterpret_cast<const bf16x8*>(ksm + k_lane + (u % kCB) * 8 * kKBlock + (u / kCB) * 128);
-}
-// V^T fragment for PV step u: key step u / 4, d-block u % 4.
-__device__ __forceinline__ bf16x8 v_frag(const char* vsm, int v_lane, int u) {
-  const char* p0 = vsm + v_lane + (u >> 2) * 4 * kVBlock + (u & 3) * 256;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0));
-  const i16x4 hi =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p0 + 2 * kVBlock));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 4
-#endif
-#ifndef ATTN_MMA_PRIO
-#define ATTN_MMA_PRIO 0
-#endif
-#ifndef ATTN_STEP_FENCE
-#define ATTN_STEP_FENCE 1
 #endif
 
 // LDS reads of the MFMA phase are issued as inline assembly with explicit
@@ -537,10 +515,8 @@ __device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned
     }
   }
   if constexpr (F + ATTN_PREFETCH < Frags<BN>::kTotal) issue_frag<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
-#if ATTN_STEP_FENCE
-  // Keep each step's VALU work beside its MFMA.
+  // Keep each step's work beside its MFMA.
   __builtin_amdgcn_sched_barrier(0);
-#endif
   if constexpr (F + 1 < Frags<BN>::kTotal)
     mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel);
 }
@@ -592,13 +568,7 @@ __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, 
                                            int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
                                            const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
                                            float alpha, bool rescale, f32x4& lacc, const bf16x8& sel) {
-#if ATTN_MMA_PRIO
-  __builtin_amdgcn_s_setprio(ATTN_MMA_PRIO);
-#endif
   mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
-#if ATTN_MMA_PRIO
-  __builtin_amdgcn_s_setprio(0);
-#endif
   wait_mem();
   barrier();
 }
