@@ -9,8 +9,13 @@
 // Chapters 6-7 (K and V move through separate double buffers, and the
 // next tile's QK^T is issued while the current tile's softmax runs).
 //
+// Two kernels: attn_fwd_kernel (four waves, one 128-row query tile per
+// workgroup, for small grids) and attn_fwd_pingpong_kernel (eight waves in
+// two phase-shifted groups, two query tiles sharing each K/V tile; see its
+// own comment).
+//
 // gfx950 mapping (not the article's B200 mapping):
-//  * Workgroup = 4 wave64s; wave w owns query rows 32w..32w+31 of the tile.
+//  * Each wave owns 32 query rows (rows 32w..32w+31 of its group's tile).
 //  * Scores are computed transposed, S^T = K . Q^T, on
 //    v_mfma_f32_32x32x16_bf16: the accumulator of a 32x32 block gives lane
 //    l the column l%32 (one query) and rows 8j + 4*(l/32) + i (keys), so a
