@@ -53,8 +53,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -64,7 +62,6 @@ constexpr int kBM = 128;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRebaseLog2 = 8.0f;  // rebase threshold in base-2 exponent units
-constexpr i16x2 kOnesBf16x2 = {0x3f80, 0x3f80};  // bf16 (1.0, 1.0)
 
 // Tile parameters (compile-time): keys per K/V tile and the waves per SIMD
 // the register allocation is held to.
@@ -147,59 +144,13 @@ __device__ __forceinline__ void qk_tile(const char* ksm, int k_lane, const bf16x
   }
 }
 
-// Raw row max of a score tile, over both half-waves.
-template <int BN>
-__device__ __forceinline__ float tile_max(const f32x16 (&s)[BN / 32]) {
-  float mx = -FLT_MAX;
-#pragma unroll
-  for (int cb = 0; cb < BN / 32; ++cb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[cb][i]);
-  return fmaxf(mx, __shfl_xor(mx, 32));
-}
-
-// acc + x[e] + x[e+1] for bf16 x, with exact products against (1, 1) and
-// an fp32 sum (v_dot2c_f32_bf16). The pair is rebuilt from its elements:
-// with this compiler, pairs taken from a bit-cast of the whole vector were
-// lowered to the same register for different pairs.
-__device__ __forceinline__ float add_bf16_pair(float acc, const bf16x8& x, int e) {
-  bf16x2 pair;
-  pair[0] = x[e];
-  pair[1] = x[e + 1];
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(i16x2, pair), kOnesBf16x2, acc, false);
-}
-
-// P = 2^(s*c - kept), rounded to bf16, as the PV B operand; returns this
-// half-wave's sum of the ROUNDED values, so that O is normalised by exactly
-// the weights its P.V used (the output is then a convex combination of V
-// rows; normalising by the unrounded sum leaves a bias when a few large P
-// round the same way). Step t's operand: slots 0..3 <- block t/2,
-// j = 2(t%2); slots 4..7 <- j = 2(t%2)+1.
-template <int BN>
-__device__ __forceinline__ float exp_tile(const f32x16 (&s)[BN / 32], float c, float kept,
-                                          bf16x8 (&pf)[BN / 16]) {
-#pragma unroll
-  for (int cb = 0; cb < BN / 32; ++cb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][4 * j + i], c, -kept));
-        pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] = (__bf16)p;
-      }
-  float ps0 = 0.0f, ps1 = 0.0f;
-#pragma unroll
-  for (int t = 0; t < BN / 16; ++t) {
-    ps0 = add_bf16_pair(ps0, pf[t], 0);
-    ps1 = add_bf16_pair(ps1, pf[t], 2);
-    ps0 = add_bf16_pair(ps0, pf[t], 4);
-    ps1 = add_bf16_pair(ps1, pf[t], 6);
-  }
-  return ps0 + ps1;
-}
-
-// P = 2^(s*c - kept), rounded to bf16, as the PV B operand (layout as in
-// exp_tile), without a row sum.
+// P = 2^(s*c - kept), rounded to bf16, as the PV B operand: step t's
+// operand takes slots 0..3 from score block t/2, j = 2(t%2), and slots 4..7
+// from j = 2(t%2)+1 (keys 16t + 4h + 0..3 and 16t + 8 + 4h + 0..3). The row
+// sum is taken from these rounded values on the matrix pipe (make_selector),
+// so O is normalised by exactly the weights its P.V used: the output is a
+// convex combination of V rows (normalising by the unrounded sum leaves a
+// bias when a few large P round the same way).
 template <int BN>
 __device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, float kept,
                                            bf16x8 (&pf)[BN / 16]) {
@@ -237,10 +188,27 @@ __device__ __forceinline__ float tile_max_swap(const f32x16 (&s)[BN / 32]) {
   return max_with_other_half(mx);
 }
 
+// A operand of the row-sum MFMA. v_mfma_f32_16x16x32_bf16 takes a PV
+// fragment as its B operand: lane l holds 8 keys of query l % 32, in the
+// 16x16x32 layout column l % 16 and k-group l / 16 (groups 0 and 2 belong to
+// query c = l % 16, groups 1 and 3 to query c + 16). Selector row r has ones
+// on the groups of query c (r = 0, 8) or c + 16 (r = 4, 12) and zeros
+// elsewhere; output row 4 * (l / 16) of column l % 16 then lands in lane l,
+// register 0, as the sum over the step's 16 keys for query l % 32.
+// Registers 1-3 of the accumulator stay 0.
+__device__ __forceinline__ bf16x8 make_selector(int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  const bool on = ((r == 0 || r == 8) && !(g & 1)) || ((r == 4 || r == 12) && (g & 1));
+  bf16x8 sel;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(on ? 1.0f : 0.0f);
+  return sel;
+}
+
 // O^T[d-block b] += V^T[b, step t] . P^T[step t] for one V tile.
 template <int BN>
 __device__ __forceinline__ void pv_tile(const char* vsm, int v_lane, const bf16x8 (&pf)[BN / 16],
-                                        f32x16 (&acc)[4]) {
+                                        f32x16 (&acc)[4], f32x4& lacc, const bf16x8& sel) {
 #pragma unroll
   for (int t = 0; t < BN / 16; ++t) {
 #pragma unroll
@@ -254,13 +222,15 @@ __device__ __forceinline__ void pv_tile(const char* vsm, int v_lane, const bf16x
       acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pf[t],
                                                        acc[b], 0, 0, 0);
     }
+    // the row sum of the same rounded P (see make_selector)
+    lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pf[t], lacc, 0, 0, 0);
   }
 }
 
 // Online-softmax base update for a new tile max (raw units): rebase when
 // the scaled max exceeds the kept base by >= 8, rescaling O and the row sum
 // only if some lane of the wave rebased.
-__device__ __forceinline__ void update_base(float raw_max, float c, float& kept, float& lsum,
+__device__ __forceinline__ void update_base(float raw_max, float c, float& kept, f32x4& lacc,
                                             f32x16 (&acc)[4]) {
   const float cand = fmaxf(kept, raw_max * c);
   const bool need = (cand - kept) >= kRebaseLog2;
@@ -270,7 +240,7 @@ __device__ __forceinline__ void update_base(float raw_max, float c, float& kept,
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
-    lsum *= alpha;
+    lacc[0] *= alpha;
     kept = need ? cand : kept;
   }
 }
@@ -285,19 +255,20 @@ __device__ __forceinline__ void kv_iteration(int jt, int ntiles, const char* kg,
                                              char* k_next, char* v_cur, char* v_next, int k_lane,
                                              int v_lane, const bf16x8 (&qf)[8], float c,
                                              const f32x16 (&s)[BN / 32], f32x16 (&sn)[BN / 32],
-                                             f32x16 (&acc)[4], float& kept, float& lsum) {
+                                             f32x16 (&acc)[4], float& kept, f32x4& lacc,
+                                             const bf16x8& sel) {
   constexpr int kTileBytes = BN * kD * 2;
   if (jt + 2 < ntiles) load_tile<BN, kKBlock>(kg + int64_t(jt + 2) * kTileBytes, kfill, k_cur, wave);
   if (jt + 1 < ntiles) load_tile<BN, kVBlock>(vg + int64_t(jt + 1) * kTileBytes, vfill, v_next, wave);
 
   bf16x8 pf[BN / 16];
-  lsum += exp_tile<BN>(s, c, kept, pf);
+  exp_tile_p<BN>(s, c, kept, pf);
   // QK^T of the next tile, issued without a branch so it can interleave
   // with the exponentials above; on the last tile it reads a stale (but
   // in-bounds) buffer and its result is dropped.
   qk_tile<BN>(k_next, k_lane, qf, sn);
-  pv_tile<BN>(v_cur, v_lane, pf, acc);
-  if (jt + 1 < ntiles) update_base(tile_max<BN>(sn), c, kept, lsum, acc);
+  pv_tile<BN>(v_cur, v_lane, pf, acc, lacc, sel);
+  if (jt + 1 < ntiles) update_base(tile_max_swap<BN>(sn), c, kept, lacc, acc);
   __syncthreads();  // K(jt+2), V(jt+1) landed; K(jt+1), V(jt) are free
 }
 
@@ -363,26 +334,27 @@ void attn_fwd_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
   float kept = -FLT_MAX;  // kept row max, base-2 units of scaled scores
-  float lsum = 0.0f;      // this half-wave's share of the row sum
+  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in register 0 (see make_selector)
+  const bf16x8 sel = make_selector(lane);
 
   f32x16 s0[BN / 32], s1[BN / 32];
   __syncthreads();  // K0, V0 (and K1) are in LDS
   qk_tile<BN>(kb0, k_lane, qf, s0);
-  update_base(tile_max<BN>(s0), c, kept, lsum, acc);
+  update_base(tile_max_swap<BN>(s0), c, kept, lacc, acc);
   __syncthreads();  // everyone is done reading K0
 
   // Iterations alternate the roles of the two K buffers, the two V buffers
   // and the two score register sets.
   for (int jt = 0; jt < ntiles; jt += 2) {
     kv_iteration<BN>(jt, ntiles, kg, vg, kfill, vfill, wave, kb0, kb1, vb0, vb1, k_lane, v_lane, qf,
-                     c, s0, s1, acc, kept, lsum);
+                     c, s0, s1, acc, kept, lacc, sel);
     if (jt + 1 >= ntiles) break;
     kv_iteration<BN>(jt + 1, ntiles, kg, vg, kfill, vfill, wave, kb1, kb0, vb1, vb0, k_lane, v_lane,
-                     qf, c, s1, s0, acc, kept, lsum);
+                     qf, c, s1, s0, acc, kept, lacc, sel);
   }
 
   // Epilogue: O = O^T / l -> bf16; lane holds dims 32b + 8j + 4h + 0..3.
-  const float ltot = lsum + __shfl_xor(lsum, 32);
+  const float ltot = lacc[0];
   const float inv = 1.0f / ltot;
   __bf16* orow = o + head + int64_t(qrow) * kD;
 #pragma unroll
@@ -698,22 +670,8 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
   float kept = -FLT_MAX;
-  // Row sum: register 0 of lacc, accumulated on the matrix pipe by
-  // v_mfma_f32_16x16x32_bf16 with the selector `sel` as A operand. The
-  // B operand is a PV fragment: lane l holds 8 keys of query l % 32, in the
-  // 16x16x32 layout column l % 16 and k-group l / 16 (groups 0 and 2 belong
-  // to query c = l % 16, groups 1 and 3 to query c + 16). Selector row r
-  // has ones on the groups of query c (r = 0, 8) or c + 16 (r = 4, 12) and
-  // zeros elsewhere; output row 4 * (l / 16) of column l % 16 then lands in
-  // lane l, register 0, as the sum for query l % 32. Registers 1-3 stay 0.
-  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};
-  bf16x8 sel;
-  {
-    const int r = lane & 15, g = lane >> 4;
-    const bool on = ((r == 0 || r == 8) && !(g & 1)) || ((r == 4 || r == 12) && (g & 1));
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sel[e] = (__bf16)(on ? 1.0f : 0.0f);
-  }
+  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in register 0 (see make_selector)
+  const bf16x8 sel = make_selector(lane);
   f32x16 s[BN / 32];
   bf16x8 pf[BN / 16];
 #pragma unroll
