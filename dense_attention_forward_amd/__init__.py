@@ -4,8 +4,8 @@
 kernel through the C ABI of ``include/attn_fwd.h``.
 """
 from ._lib import (VARIANT_AUTO, VARIANT_PAIR256, VARIANT_TILE128, AttnError, HEAD_DIM, LIB_PATH,
-                   attn_fwd_raw, check, default_scale, forward, lib, pick, status_str)
+                   attn_fwd_raw, check, default_scale, forward, lib, mfma_rate, pick, status_str)
 
 __all__ = ["VARIANT_AUTO", "VARIANT_PAIR256", "VARIANT_TILE128", "AttnError", "HEAD_DIM",
-           "LIB_PATH", "attn_fwd_raw", "check", "default_scale", "forward", "lib", "pick",
-           "status_str"]
+           "LIB_PATH", "attn_fwd_raw", "check", "default_scale", "forward", "lib", "mfma_rate",
+           "pick", "status_str"]

@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
             l.attn_fwd_check.restype = i
             l.attn_status_str.argtypes = [i]
             l.attn_status_str.restype = ctypes.c_char_p
+            l.attn_mfma_rate.argtypes = [vp, vp, i, i, vp]
+            l.attn_mfma_rate.restype = i
             _lib = l
         return _lib
 
@@ -119,3 +121,26 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None, variant: in
     if st != ATTN_OK:
         raise AttnError(st, status_str(st))
     return out, lse
+
+
+MFMA_RATE_FLOPS_PER_WG_ITER = 4 * 16 * 32768  # 4 waves x 16 MFMAs x 2*32*32*16
+
+
+def mfma_rate(operands, sink, workgroups: int, iters: int) -> int:
+    """Enqueue the MFMA-rate stream (include/attn_mfma_rate.h) on torch's current
+    stream: `operands` a device tensor of at least workgroups*256*128 bytes,
+    `sink` a float32 device tensor of at least workgroups*256 elements.
+    Returns the FLOPs the launch performs; raises AttnError on a bad status."""
+    import torch
+
+    if not (operands.is_cuda and sink.is_cuda and sink.dtype == torch.float32):
+        raise ValueError("operands and a float32 sink must be device tensors")
+    if not (operands.is_contiguous() and sink.is_contiguous()):
+        raise ValueError("operands and sink must be contiguous")
+    if operands.numel() * operands.element_size() < workgroups * 256 * 128 or sink.numel() < workgroups * 256:
+        raise ValueError("operands or sink too small for this many workgroups")
+    stream = torch.cuda.current_stream(operands.device).cuda_stream
+    st = lib().attn_mfma_rate(operands.data_ptr(), sink.data_ptr(), int(workgroups), int(iters), stream)
+    if st != ATTN_OK:
+        raise AttnError(st, status_str(st))
+    return workgroups * iters * MFMA_RATE_FLOPS_PER_WG_ITER

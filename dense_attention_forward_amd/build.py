@@ -16,8 +16,8 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libattn_fwd.so"
 
-SOURCES = [CSRC / "attn_fwd_kernel.hip", CSRC / "attn_fwd_abi.cpp"]
-HEADERS = [ROOT / "include" / "attn_fwd.h", CSRC / "attn_fwd_launch.h"]
+SOURCES = [CSRC / "attn_fwd_kernel.hip", CSRC / "attn_fwd_abi.cpp", CSRC / "attn_mfma_rate.hip"]
+HEADERS = [ROOT / "include" / "attn_fwd.h", ROOT / "include" / "attn_mfma_rate.h", CSRC / "attn_fwd_launch.h"]
 
 ARCH = "gfx950"
 # Packed-FP32 VALU forms are disabled for all device code.

@@ -147,3 +147,15 @@ def test_pick(lib):
     assert lib.pick(4, 16, 4096) == lib.VARIANT_PAIR256
     assert lib.pick(2, 16, 8192) == lib.VARIANT_PAIR256
     assert lib.pick(1, 16, 16384) == lib.VARIANT_PAIR256
+
+
+def test_mfma_rate_rejects_before_launch(lib):
+    """The MFMA-rate probe validates its arguments before any HIP call."""
+    r = lib.lib().attn_mfma_rate
+    assert r(0, L, 8, 10, 0) == 1
+    assert r(Q, 0, 8, 10, 0) == 1
+    assert r(Q + 8, L, 8, 10, 0) == 3
+    assert r(Q, L + 2, 8, 10, 0) == 3
+    assert r(Q, L, 0, 10, 0) == 2
+    assert r(Q, L, 8, 0, 0) == 2
+    assert r(Q, L, 2 ** 30, 10, 0) == 2
