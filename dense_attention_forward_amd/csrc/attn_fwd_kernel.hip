@@ -151,7 +151,31 @@ __device__ __forceinline__ void qk_tile(const char* ksm, int k_lane, const bf16x
 // so O is normalised by exactly the weights its P.V used: the output is a
 // convex combination of V rows (normalising by the unrounded sum leaves a
 // bias when a few large P round the same way).
-template <int BN>
+// Software 2^x (the article's Chapter 9 idea: compute part of the
+// exponentials on the FMA pipe instead of the exponent unit), written from
+// 2^x = 2^n * 2^f with n = floor(x), f = x - n in [0, 1) and 2^f by a
+// degree-3 polynomial in f. The coefficients minimise the maximum relative
+// error on [0, 1] (Remez exchange, with c0 pinned to 1 so integer arguments
+// are exact): 8.6e-5 with these float32 values, far below the 2^-9 of the
+// bf16 rounding that follows. They are produced by exp2_poly_fit.py beside
+// this file. Arguments below -256 give 0, like the flushing exponent unit.
+constexpr float kExp2C0 = 1.0f;
+constexpr float kExp2C1 = 0.6951163411140442f;
+constexpr float kExp2C2 = 0.22764700651168823f;
+constexpr float kExp2C3 = 0.07706519961357117f;
+__device__ __forceinline__ float exp2_poly(float x) {
+  const float n = fmaxf(__builtin_floorf(x), -256.0f);
+  const float f = x - n;
+  float p = __builtin_fmaf(kExp2C3, f, kExp2C2);
+  p = __builtin_fmaf(p, f, kExp2C1);
+  p = __builtin_fmaf(p, f, kExp2C0);
+  return __builtin_ldexpf(p, int(n));
+}
+
+// kEmuEvery = 0: every exponential on v_exp_f32. kEmuEvery = k: one element
+// in k (those with index % k == k - 1 inside each score block) takes
+// exp2_poly instead.
+template <int BN, int kEmuEvery = 0>
 __device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, float kept,
                                            bf16x8 (&pf)[BN / 16]) {
 #pragma unroll
@@ -160,7 +184,9 @@ __device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, 
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][4 * j + i], c, -kept));
+        const float x = __builtin_fmaf(s[cb][4 * j + i], c, -kept);
+        const bool emu = kEmuEvery > 0 && (4 * j + i) % (kEmuEvery > 0 ? kEmuEvery : 1) == kEmuEvery - 1;
+        const float p = emu ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
         pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] = (__bf16)p;
       }
 }
@@ -553,7 +579,7 @@ __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, 
 // Softmax phase i: group B first issues the loads of K(i+2) (into the
 // buffer K(i) left) and V(i+1); then the base update, whose factor for O
 // (already holding PV(i-1)) the next MFMA phase applies, and P(i).
-template <int BN>
+template <int BN, int kEmuEvery>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
                                            char* vcur, float c, const f32x16 (&s)[BN / 32],
@@ -572,7 +598,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
   }
   alpha = base_update_alpha(tile_max_swap<BN>(s), c, kept);
   rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-  exp_tile_p<BN>(s, c, kept, pf);
+  exp_tile_p<BN, kEmuEvery>(s, c, kept, pf);
   // P must be complete here, not computed after the barrier where it is
   // first used: the overlap of this phase with the other group's MFMAs
   // depends on it.
@@ -600,7 +626,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 // The MFMA phase also takes the row sum of the P it consumes, on the matrix
 // pipe; the softmax phase keeps the row max, the base update and the
 // exponentials.
-template <int BN>
+template <int BN, int kEmuEvery>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
                               const char* __restrict__ v, __bf16* __restrict__ o,
@@ -691,7 +717,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   barrier();
   float alpha;
   bool rescale;
-  pp_v_phase<BN>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha, rescale,
+  pp_v_phase<BN, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha, rescale,
                  kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
@@ -699,7 +725,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
     pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
     if (i == ntiles) break;
-    pp_v_phase<BN>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
+    pp_v_phase<BN, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                    rescale, kept);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
@@ -739,13 +765,15 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   constexpr int BN = ATTN_BN;
   const int qtiles = p.S / kBM;
   const float c = p.scale * kLog2e;
-  if (p.variant == ATTN_VARIANT_PAIR256) {
+  if (p.variant == ATTN_VARIANT_PAIR256 || p.variant == ATTN_VARIANT_PAIR256_EXP2EMU) {
     const int npairs = (qtiles + 1) / 2;
     const int nwg = int(int64_t(p.B) * p.H * npairs);
-    hipLaunchKernelGGL(attn_fwd_pingpong_kernel<ATTN_PP_BN>, dim3(nwg), dim3(2 * kThreads), 0, stream,
-                       static_cast<const uint4*>(p.q), static_cast<const char*>(p.k),
-                       static_cast<const char*>(p.v), static_cast<__bf16*>(p.o), p.lse, p.S,
-                       qtiles, npairs, nwg, c);
+    // PAIR256_EXP2EMU: one exponential in four on the FMA pipe
+    auto kernel = p.variant == ATTN_VARIANT_PAIR256 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 0>
+                                                    : attn_fwd_pingpong_kernel<ATTN_PP_BN, 4>;
+    hipLaunchKernelGGL(kernel, dim3(nwg), dim3(2 * kThreads), 0, stream, static_cast<const uint4*>(p.q),
+                       static_cast<const char*>(p.k), static_cast<const char*>(p.v),
+                       static_cast<__bf16*>(p.o), p.lse, p.S, qtiles, npairs, nwg, c);
     return hipGetLastError();
   }
   const int nwg = p.B * p.H * qtiles;

@@ -59,11 +59,17 @@ enum attn_status {
  *                          tiles of one head that share every K/V tile, the
  *                          two 4-wave groups phase-shifted so one runs its
  *                          matrix products while the other runs its softmax
+ *   ATTN_VARIANT_PAIR256_EXP2EMU : PAIR256 with one exponential in four
+ *                          computed by a polynomial on the FMA pipe instead
+ *                          of the exponent unit (the article's Chapter 9
+ *                          "software approximations"); for measurement,
+ *                          never picked by attn_fwd
  */
 enum attn_variant {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_TILE128 = 1,
-  ATTN_VARIANT_PAIR256 = 2
+  ATTN_VARIANT_PAIR256 = 2,
+  ATTN_VARIANT_PAIR256_EXP2EMU = 3
 };
 
 /*

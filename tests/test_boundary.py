@@ -133,7 +133,7 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
 
 
 def test_variant_rejected_before_launch(lib):
-    for bad in (-1, 3, 99):
+    for bad in (-1, 4, 99):
         assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, D, SC, 0, variant=bad) == 7
     # a valid variant with bad arguments still reports the argument error
     assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, 64, SC, 0, variant=2) == 2
