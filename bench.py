@@ -34,9 +34,13 @@ KERNEL_SOURCES = [ROOT / "dense_attention_forward_amd" / "csrc" / n
 
 
 def kernel_digest() -> str:
+    """Hash of the kernel sources' code: // comments removed and whitespace
+    collapsed, so edits to comments or layout keep the measured counters
+    valid while any code change invalidates them."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        h.update(p.read_bytes())
+        code = re.sub(r"//[^\n]*", "", p.read_text())
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -576,9 +576,9 @@ __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, 
   barrier();
 }
 
-// Softmax phase i: group B first issues the loads of K(i+2) (into the
-// buffer K(i) left) and V(i+1); then the base update, whose factor for O
-// (already holding PV(i-1)) the next MFMA phase applies, and P(i).
+// Softmax phase i: first this group's share of the tile loads (below), then
+// the row max and base update, whose factor for O (already holding
+// PV(i-1)) the next MFMA phase applies, and P(i).
 template <int BN, int kEmuEvery>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                            const char* vg, int kfill, int vfill, char* kfree,
@@ -717,16 +717,16 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   barrier();
   float alpha;
   bool rescale;
-  pp_v_phase<BN, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha, rescale,
-                 kept);
+  pp_v_phase<BN, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha,
+                            rescale, kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
-    char* const v_other = odd ? vb0 : vb1;  // V(i-1), then V(i+1)
+    char* const v_other = odd ? vb0 : vb1;  // V(i-1); group A then loads V(i) into the other buffer
     pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
     if (i == ntiles) break;
-    pp_v_phase<BN, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
-                   rescale, kept);
+    pp_v_phase<BN, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s,
+                              pf, alpha, rescale, kept);
   }
   if (group == 0) barrier();  // matches B's phase-shift barrier
 
