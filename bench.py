@@ -83,11 +83,12 @@ def time_workload(daf, torch, w, steps: int, warmup: int):
 
 
 def sustained_mfma(daf, torch, reps: int = 5, iters: int = 2000):
-    """Rate of a pure v_mfma_f32_32x32x16_bf16 stream (no memory in the loop)
-    on N(0,1) bf16 operands, the workloads' distribution, 8 waves per SIMD on
-    every CU. Under sustained MFMA load the clock is set by power, which
-    depends on operand toggling, so this is what the matrix cores sustain on
-    such data; the published peak assumes the top clock."""
+    """Rate of a pure v_mfma_f32_16x16x32_bf16 stream (no memory in the loop;
+    the instruction of the eight-wave kernel) on N(0,1) bf16 operands, the
+    workloads' distribution, 8 workgroups of 4 waves per CU. Under sustained
+    MFMA load the clock is set by power, which depends on operand toggling,
+    so this is what the matrix cores sustain on such data; the published
+    peak assumes the top clock."""
     dev = torch.device("cuda", 0)
     wgs = torch.cuda.get_device_properties(dev).multi_processor_count * 8
     gen = torch.Generator(device=dev).manual_seed(7)
@@ -107,8 +108,8 @@ def sustained_mfma(daf, torch, reps: int = 5, iters: int = 2000):
     rates.sort()
     return {"value": round(rates[-1], 1), "median": round(rates[len(rates) // 2], 1), "unit": "TFLOP/s",
             "operands": "bf16 N(0,1)", "launches": reps,
-            "kernel": "attn_mfma_rate: v_mfma_f32_32x32x16_bf16 stream from registers, 4 accumulators, "
-                      "8 waves per SIMD on every CU"}
+            "kernel": "attn_mfma_rate: v_mfma_f32_16x16x32_bf16 stream from registers, 8 accumulators "
+                      "in VGPRs, 8 workgroups of 4 waves per CU"}
 
 
 def cpu_baseline(w, max_heads: int):

@@ -123,7 +123,7 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None, variant: in
     return out, lse
 
 
-MFMA_RATE_FLOPS_PER_WG_ITER = 4 * 16 * 32768  # 4 waves x 16 MFMAs x 2*32*32*16
+MFMA_RATE_FLOPS_PER_WG_ITER = 4 * 32 * 16384  # 4 waves x 32 MFMAs x 2*16*16*32
 
 
 def mfma_rate(operands, sink, workgroups: int, iters: int) -> int:

@@ -5,7 +5,8 @@
 // inside it, online softmax of section B), Chapter 8 (base-2 exponent with
 // scale*log2(e) folded into the score scale; the max is taken over raw
 // scores and scaled once), Chapter 11 (the O accumulator is rescaled only
-// when a row's max grows by >= 8 in base-2 units, decided per wave),
+// when a row's max grows past a threshold, decided per wave; the article's
+// threshold is 8 in base-2 units, these kernels use 16, see kRebaseLog2),
 // Chapters 6-7 (K and V move through separate double buffers, and the
 // next tile's QK^T is issued while the current tile's softmax runs).
 //
@@ -61,7 +62,13 @@ constexpr int kD = 128;         // head dimension
 constexpr int kBM = 128;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kRebaseLog2 = 8.0f;  // rebase threshold in base-2 exponent units
+// Rebase threshold in base-2 exponent units: a row keeps its base until its
+// max exceeds it by this much, so unnormalised P stays below 2^16 and O
+// below 2^16 * S * max|V| (fp32 overflows only for |V| beyond ~2^80). A
+// rescale of O costs 65 serial VALU instructions in the MFMA phase; 16
+// instead of the article's 8 makes it rare on peaked rows (normal Q and K
+// of standard deviation 2 at S = 8192: from 17% of tiles per wave to 0.1%).
+constexpr float kRebaseLog2 = 16.0f;
 
 // Tile parameters (compile-time): keys per K/V tile and the waves per SIMD
 // the register allocation is held to.
@@ -75,17 +82,28 @@ constexpr float kRebaseLog2 = 8.0f;  // rebase threshold in base-2 exponent unit
 // LDS tile layouts. A K or V tile of BN key rows is BN/4 blocks; block j
 // holds rows 4j..4j+3 (4 x 256 bytes) as 64 slots of 16 bytes.
 //
-// K: the slot of (row 4j + rr, 16-byte chunk 2kk + h) is rr + 4h + 8kk, and
-// blocks are 1088 bytes apart (64 bytes of padding). The QK^T A-operand
-// read of step kk has lane (n, h) at block n/4, slot (n%4) + 4h + 8kk: 16
-// lanes of one half-wave cover 4 blocks x 4 rows, whose bank groups
-// 4*(block%4) + rr + 4h + 8kk (mod 16) are all distinct.
-constexpr int kKBlock = 1088;
-// V: the slot of (row 4j + q, chunk 4b + x) is 16b + 4q + x, blocks 1 KB
-// apart. The transposed read of d-block b touches, per half-wave, the 4
-// rows of one block at chunks 4b..4b+3: 16 consecutive slots, all banks
+// K: the slot of (row 4j + rr, 16-byte chunk c) is rr + 4c, with padding
+// between blocks. A ds_read_b128 of 16 lanes covers 4 blocks x 4 rows at
+// one chunk: lanes n of the four-wave kernel (rows n of 32) and lanes l%16
+// of a 16-lane group of the eight-wave kernel (rows 16kb + l%16). The
+// padding of each kernel was chosen by measurement, as the one that shows
+// no LDS bank conflicts (SQ_LDS_BANK_CONFLICT = 0) for its read pattern:
+// 64 bytes (1088-byte blocks) for the four-wave kernel, 128 bytes (1152)
+// for the eight-wave one. With 64 bytes the eight-wave pattern conflicts
+// 2-way on every read, and with 128 bytes the four-wave one conflicts too.
+// (If a bank were simply (address / 4) % 64, 64 bytes would suit both.)
+constexpr int kKBlock = 1088;      // four-wave kernel
+constexpr int kKBlockPair = 1152;  // eight-wave kernel
+// V: the slot of (row 4j + q, chunk 4b + x) is 16b + 4q + x, blocks 1056
+// bytes apart (32 bytes of padding). A transposed read (ds_read_b64_tr_b16)
+// is served 32 lanes at a time, 256 bytes over the 64 banks; each 16-lane
+// group reads 32 bytes from each of the 4 rows of one block (8 banks per
+// row, rows 64 bytes apart). In the four-wave kernel the two groups of a
+// half-wave read the two 16-column halves of the same rows; in the
+// eight-wave kernel they read the same columns of consecutive blocks, which
+// the padding shifts by 8 banks. Either way the 32 lanes meet every bank
 // once.
-constexpr int kVBlock = 1024;
+constexpr int kVBlock = 1056;
 
 // Global byte offset (within a 4-row block) that lane l fetches so that its
 // 16 bytes land in slot l.
@@ -102,7 +120,7 @@ __device__ __forceinline__ int v_fill_offset(int l) {
 // by before the next P.V (1 for rows that keep their base; exactly 1.0, so
 // multiplying by it changes nothing).
 __device__ __forceinline__ float base_update_alpha(float raw_max, float c, float& kept) {
-  const float cand = fmaxf(kept, raw_max * c);
+  const float cand = __builtin_elementwise_maximum(kept, raw_max * c);
   const bool need = (cand - kept) >= kRebaseLog2;
   const float alpha = need ? __builtin_amdgcn_exp2f(kept - cand) : 1.0f;
   kept = need ? cand : kept;
@@ -172,10 +190,7 @@ __device__ __forceinline__ float exp2_poly(float x) {
   return __builtin_ldexpf(p, int(n));
 }
 
-// kEmuEvery = 0: every exponential on v_exp_f32. kEmuEvery = k: one element
-// in k (those with index % k == k - 1 inside each score block) takes
-// exp2_poly instead.
-template <int BN, int kEmuEvery = 0>
+template <int BN>
 __device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, float kept,
                                            bf16x8 (&pf)[BN / 16]) {
 #pragma unroll
@@ -183,12 +198,9 @@ __device__ __forceinline__ void exp_tile_p(const f32x16 (&s)[BN / 32], float c, 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = __builtin_fmaf(s[cb][4 * j + i], c, -kept);
-        const bool emu = kEmuEvery > 0 && (4 * j + i) % (kEmuEvery > 0 ? kEmuEvery : 1) == kEmuEvery - 1;
-        const float p = emu ? exp2_poly(x) : __builtin_amdgcn_exp2f(x);
-        pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] = (__bf16)p;
-      }
+      for (int i = 0; i < 4; ++i)
+        pf[2 * cb + (j >> 1)][(j & 1) * 4 + i] =
+            (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][4 * j + i], c, -kept));
 }
 
 // The other half-wave's value of x (lane l <-> lane l ^ 32), through
@@ -205,13 +217,18 @@ __device__ __forceinline__ float max_with_other_half(float x) {
 // by contract) and the half-wave exchange on v_permlane32_swap.
 template <int BN>
 __device__ __forceinline__ float tile_max_swap(const f32x16 (&s)[BN / 32]) {
-  float mx = -FLT_MAX;
+  // Two running maxima, each taking two values per v_maximum3_f32: 33
+  // instructions for a lane's 2 * BN scores, on chains half as long.
+  float m0 = __builtin_elementwise_maximum(s[0][0], s[0][1]);
+  float m1 = __builtin_elementwise_maximum(s[0][2], s[0][3]);
 #pragma unroll
   for (int cb = 0; cb < BN / 32; ++cb)
 #pragma unroll
-    for (int i = 0; i < 16; i += 2)
-      mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[cb][i], s[cb][i + 1]));
-  return max_with_other_half(mx);
+    for (int i = cb == 0 ? 4 : 0; i < 16; i += 4) {
+      m0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, s[cb][i]), s[cb][i + 1]);
+      m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, s[cb][i + 2]), s[cb][i + 3]);
+    }
+  return max_with_other_half(__builtin_elementwise_maximum(m0, m1));
 }
 
 // A operand of the row-sum MFMA. v_mfma_f32_16x16x32_bf16 takes a PV
@@ -254,11 +271,11 @@ __device__ __forceinline__ void pv_tile(const char* vsm, int v_lane, const bf16x
 }
 
 // Online-softmax base update for a new tile max (raw units): rebase when
-// the scaled max exceeds the kept base by >= 8, rescaling O and the row sum
+// the scaled max exceeds the kept base by >= kRebaseLog2, rescaling O and the row sum
 // only if some lane of the wave rebased.
 __device__ __forceinline__ void update_base(float raw_max, float c, float& kept, f32x4& lacc,
                                             f32x16 (&acc)[4]) {
-  const float cand = fmaxf(kept, raw_max * c);
+  const float cand = __builtin_elementwise_maximum(kept, raw_max * c);
   const bool need = (cand - kept) >= kRebaseLog2;
   if (__any(need)) {
     const float alpha = need ? __builtin_amdgcn_exp2f(kept - cand) : 1.0f;
@@ -441,15 +458,48 @@ __device__ __forceinline__ void lgkm_wait() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Fragment f of an MFMA phase: f < kK is QK step f (K tile), then PV step
-// f - kK (V tile). A K fragment is one LDS read, a V fragment two.
+// Ring of LDS operand fragments of an MFMA phase, ATTN_PREFETCH deep.
+struct MmaRing {
+  u32x4 k[ATTN_PREFETCH];
+  u32x2 vlo[ATTN_PREFETCH], vhi[ATTN_PREFETCH];
+};
+
+// ---------------------------------------------------------------------------
+// Eight-wave kernel (variants PAIR256, PAIR256_EXP2EMU) on
+// v_mfma_f32_16x16x32_bf16. Same LDS layouts and tile loads as the four-wave
+// kernel; a stream of 16x16x32 MFMAs sustains a markedly higher rate on
+// gfx950 than one of 32x32x16 MFMAs, though both do 1024 FLOPs per cycle
+// per SIMD on paper (about 1.95 against 1.55-1.77 PFLOP/s on N(0,1) bf16
+// operands, the lower figure with two waves interleaving MFMAs on a SIMD).
+//
+// D[16x16] += A[16x32] . B[32x16]: lane l holds row l%16 of A and column
+// l%16 of B, each with k = 8g .. 8g+7 where g = l/16, and column l%16 of D
+// at rows 4g .. 4g+3. Each wave owns 32 queries as two 16-query blocks qb.
+//  * S^T = K . Q^T per 16-key block kb: A = K rows (keys) from LDS, B = Q
+//    (registers). Lane l then holds query 16qb + l%16, keys 16kb + 4g + i.
+//    A query's scores are spread over the four lane groups g, so the row
+//    max ends with two exchanges (v_permlane16_swap, v_permlane32_swap).
+//  * O^T += V^T . P^T per 32-key step t and 16-column block db of d. The k
+//    slot 8g + j of both operands stands for key 32t + 4g + j (j < 4) or
+//    32t + 16 + 4g + (j - 4) (j >= 4): exactly the keys the lane's two
+//    score blocks 2t and 2t+1 hold, so P needs no data movement. V^T is
+//    gathered for those keys with two ds_read_b64_tr_b16 per fragment.
+//  * The row sum is a 16x16x32 MFMA of an all-ones A with the same P
+//    operand: every row of its D is the key sum of lane l's query.
+//  * Every K and V fragment read from LDS feeds the MFMAs of both query
+//    blocks, so LDS traffic per FLOP is that of the 32x32x16 kernel.
+// ---------------------------------------------------------------------------
+
+// Fragments of an MFMA phase in issue order: first the V fragments of
+// PV(i-1) (step t, d block db), then the K fragments of QK(i) (score block
+// kb, 32-dim step). PV first lets the P operands die before the scores are
+// written, which keeps the phase within the register budget.
 template <int BN>
-struct Frags {
-  static constexpr int kK = BN / 4;
-  static constexpr int kTotal = BN / 2;
-  static constexpr int ops(int f) { return f < kK ? 1 : 2; }
-  // reads issued after fragment f while it is awaited: fragments f+1 ..
-  // f+kPF-1 are in flight (the ring holds kPF fragments)
+struct Frags16 {
+  static constexpr int kKB = BN / 16;       // 16-key score blocks per tile
+  static constexpr int kV = BN / 4;         // V fragments: BN/32 steps x 8 d blocks
+  static constexpr int kTotal = kV + kKB * 4;
+  static constexpr int ops(int f) { return f < kV ? 2 : 1; }
   static constexpr int after(int f, int pf) {
     int n = 0;
     for (int g = f + 1; g < f + pf && g < kTotal; ++g) n += ops(g);
@@ -457,123 +507,155 @@ struct Frags {
   }
 };
 
-struct MmaRing {
-  u32x4 k[ATTN_PREFETCH];
-  u32x2 vlo[ATTN_PREFETCH], vhi[ATTN_PREFETCH];
-};
-
 template <int BN, int F>
-__device__ __forceinline__ void issue_frag(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
-  constexpr int kCB = BN / 32;
+__device__ __forceinline__ void issue_frag16(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
   constexpr int slot = F % ATTN_PREFETCH;
-  if constexpr (F < Frags<BN>::kK) {
-    ring.k[slot] = lds_b128<(F % kCB) * 8 * kKBlock + (F / kCB) * 128>(kaddr);
+  if constexpr (F < Frags16<BN>::kV) {
+    constexpr int db = F % 8, t = F / 8;
+    constexpr int off = t * 8 * kVBlock + 256 * (db >> 1) + 32 * (db & 1);
+    lds_tr_pair<off, off + 4 * kVBlock>(vaddr, ring.vlo[slot], ring.vhi[slot]);
   } else {
-    constexpr int u = F - Frags<BN>::kK;
-    constexpr int off = (u >> 2) * 4 * kVBlock + (u & 3) * 256;
-    lds_tr_pair<off, off + 2 * kVBlock>(vaddr, ring.vlo[slot], ring.vhi[slot]);
+    constexpr int f = F - Frags16<BN>::kV;
+    constexpr int kb = f % Frags16<BN>::kKB, step = f / Frags16<BN>::kKB;
+    ring.k[slot] = lds_b128<kb * 4 * kKBlockPair + step * 256>(kaddr);
   }
 }
 
 template <int BN, int F>
-__device__ __forceinline__ void mma_step(MmaRing& ring, unsigned kaddr, unsigned vaddr,
-                                         const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                         const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                         f32x4& lacc, const bf16x8& sel) {
-  constexpr int kCB = BN / 32;
+__device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsigned vaddr,
+                                           const bf16x8 (&qf)[2][4], f32x4 (&s)[BN / 16][2],
+                                           const bf16x8 (&pf)[2][BN / 32], f32x4 (&acc)[8][2],
+                                           f32x4 (&lacc)[2], const bf16x8& ones) {
   constexpr int slot = F % ATTN_PREFETCH;
-  constexpr int N = Frags<BN>::after(F, ATTN_PREFETCH);
-  if constexpr (F < Frags<BN>::kK) {
-    lgkm_wait<N>();
-    const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
-    // the first MFMA of each score block starts from the constant 0
-    const f32x16 zero = {};
-    s[F % kCB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[F / kCB], F < kCB ? zero : s[F % kCB],
-                                                         0, 0, 0);
-  } else {
-    constexpr int u = F - Frags<BN>::kK;
+  constexpr int N = Frags16<BN>::after(F, ATTN_PREFETCH);
+  if constexpr (F < Frags16<BN>::kV) {
+    constexpr int db = F % 8, t = F / 8;
     lgkm_wait<N>();
     const u32x4 a = __builtin_shufflevector(ring.vlo[slot], ring.vhi[slot], 0, 1, 2, 3);
-    // PV accumulates in place through a tied operand, which keeps each O
-    // accumulator in one register set (with the builtin the allocator moved
-    // all four between two sets every phase). Each accumulator is reused
-    // every fourth MFMA with exact dst/srcC overlap, which the hardware
-    // chains without wait states.
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
-                 : "+v"(acc[u & 3])
-                 : "v"(a), "v"(pf[u >> 2]));
-    // After the fourth MFMA of key step u/4, the same P fragment meets the
-    // selector operand in a 16x16x32 MFMA that adds the step's 16 keys of
-    // both half-waves into the row sum (lane l, register 0 holds the sum of
-    // query l % 32). The sum thus takes exactly the rounded P the PV used,
-    // on the matrix pipe instead of the vector ALU.
-    if constexpr ((u & 3) == 3)
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(lacc) : "v"(sel), "v"(pf[u >> 2]));
-    if constexpr (F + 1 == Frags<BN>::kTotal) {
-      // The last MFMAs' results are read by VALU code (rescale, epilogue)
-      // the compiler cannot see is dependent: give the 32x32 MFMA its
-      // write-back latency first.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]),
-                   "+v"(acc[3]), "+v"(lacc));
+    // In place through tied operands, as in the 32x32x16 kernel.
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][0]) : "v"(a), "v"(pf[0][t]));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][1]) : "v"(a), "v"(pf[1][t]));
+    if constexpr (db == 7) {
+      // Row sums of step t's P, the same rounded values the PV used. As
+      // builtins, so that the compiler's hazard checks cover any copy it
+      // makes of the operands.
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][t], lacc[qb], 0, 0, 0);
     }
+  } else {
+    constexpr int f = F - Frags16<BN>::kV;
+    constexpr int kb = f % Frags16<BN>::kKB, step = f / Frags16<BN>::kKB;
+    lgkm_wait<N>();
+    const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
+    const f32x4 zero = {};
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+      s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
+                                                          0, 0, 0);
   }
-  if constexpr (F + ATTN_PREFETCH < Frags<BN>::kTotal) issue_frag<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
-  // Keep each step's work beside its MFMA.
+  if constexpr (F + ATTN_PREFETCH < Frags16<BN>::kTotal) issue_frag16<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (F + 1 < Frags<BN>::kTotal)
-    mma_step<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel);
+  if constexpr (F + 1 < Frags16<BN>::kTotal)
+    mma_step16<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
 }
 
 template <int BN, int F>
-__device__ __forceinline__ void issue_first(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
-  issue_frag<BN, F>(ring, kaddr, vaddr);
-  if constexpr (F + 1 < ATTN_PREFETCH) issue_first<BN, F + 1>(ring, kaddr, vaddr);
+__device__ __forceinline__ void issue_first16(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
+  issue_frag16<BN, F>(ring, kaddr, vaddr);
+  if constexpr (F + 1 < ATTN_PREFETCH) issue_first16<BN, F + 1>(ring, kaddr, vaddr);
 }
 
-// The MFMA work of one phase: QK of a K tile into s, then PV of a V tile
-// into acc, with the LDS operands ATTN_PREFETCH fragments ahead of use.
+// MFMA phase i >= 1: the O rescale chosen by softmax phase i-1 (only if
+// some row of the wave rebased), PV(i-1) and QK(i), then publish this
+// wave's finished loads and pass a barrier. The epilogue and the next
+// rescale read O long after its last MFMA (the QK steps follow it).
 template <int BN>
-__device__ __forceinline__ void mma_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
-                                          const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                          const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4], float alpha,
-                                          bool rescale, f32x4& lacc, const bf16x8& sel) {
-  // O is rescaled here, in the MFMA phase, by the factor the softmax phase
-  // chose (1 for rows that kept their base), and only when some row of the
-  // wave rebased (`rescale` is wave-uniform): keeping every VALU write of O
-  // next to the MFMAs that use it lets O stay in one set of registers.
+__device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
+                                             const bf16x8 (&qf)[2][4], f32x4 (&s)[BN / 16][2],
+                                             const bf16x8 (&pf)[2][BN / 32], f32x4 (&acc)[8][2],
+                                             const float (&alpha)[2], bool rescale, f32x4 (&lacc)[2],
+                                             const bf16x8& ones) {
   if (rescale) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[b][i] *= alpha;
-    lacc[0] *= alpha;
+      for (int db = 0; db < 8; ++db) acc[db][qb] *= alpha[qb];
+      lacc[qb] *= alpha[qb];
+    }
+    // The PV MFMAs below are inline assembly, which the compiler's hazard
+    // checks do not see: give the VALU writes their wait states here.
+    asm volatile("s_nop 4" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
+                 "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]), "+v"(acc[4][0]),
+                 "+v"(acc[4][1]), "+v"(acc[5][0]), "+v"(acc[5][1]), "+v"(acc[6][0]), "+v"(acc[6][1]),
+                 "+v"(acc[7][0]), "+v"(acc[7][1]), "+v"(lacc[0]), "+v"(lacc[1]));
   }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing ring;
-  issue_first<BN, 0>(ring, kaddr, vaddr);
-  mma_step<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, sel);
-}
-
-// QK of one K tile only (first phase), same scheme with plain builtins.
-template <int BN>
-__device__ __forceinline__ void qk_only(const char* ksm, int k_lane, const bf16x8 (&qf)[8],
-                                        f32x16 (&s)[BN / 32]) {
-  qk_tile<BN>(ksm, k_lane, qf, s);
-}
-
-// MFMA phase i >= 1 of the eight-wave kernel: PV(i-1) and QK(i), then
-// publish this wave's finished loads and pass a barrier. In the last phase
-// (i == ntiles) the QK reads a stale but in-bounds buffer and its result is
-// never used; issuing it keeps the phase branch-free.
-template <int BN>
-__device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, int k_lane,
-                                           int v_lane, const bf16x8 (&qf)[8], f32x16 (&s)[BN / 32],
-                                           const bf16x8 (&pf)[BN / 16], f32x16 (&acc)[4],
-                                           float alpha, bool rescale, f32x4& lacc, const bf16x8& sel) {
-  mma_phase<BN>(kcur, vprev, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
+  issue_first16<BN, 0>(ring, kaddr, vaddr);
+  mma_step16<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
   wait_mem();
   barrier();
+}
+
+// QK of the first K tile alone, with plain builtins.
+template <int BN>
+__device__ __forceinline__ void qk16_tile(const char* ksm, int k_lane, const bf16x8 (&qf)[2][4],
+                                          f32x4 (&s)[BN / 16][2]) {
+#pragma unroll
+  for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(ksm + k_lane + kb * 4 * kKBlockPair + step * 256);
+      const f32x4 zero = {};
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
+                                                            0, 0, 0);
+    }
+}
+
+// Max of x over the four lanes l%16 + 16g that hold one query's scores.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Raw row max of query block qb over the tile: two v_maximum3 chains over
+// the lane's 4 * BN/16 scores, then the exchange between lane groups.
+template <int BN>
+__device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][2], int qb) {
+  float m0 = __builtin_elementwise_maximum(s[0][qb][0], s[0][qb][1]);
+  float m1 = __builtin_elementwise_maximum(s[0][qb][2], s[0][qb][3]);
+#pragma unroll
+  for (int kb = 1; kb < BN / 16; ++kb) {
+    m0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, s[kb][qb][0]), s[kb][qb][1]);
+    m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, s[kb][qb][2]), s[kb][qb][3]);
+  }
+  return max_over_groups(__builtin_elementwise_maximum(m0, m1));
+}
+
+// P = 2^(s*c - kept) in bf16 as PV B operands: step t of query block qb
+// takes slots 0..3 from score block 2t and slots 4..7 from block 2t+1.
+// kEmuEvery = 0: every exponential on v_exp_f32. kEmuEvery = k: one element
+// in k (those with (4 kb + i) % k == k - 1) takes exp2_poly instead.
+template <int BN, int kEmuEvery>
+__device__ __forceinline__ void exp16_tile_p(const f32x4 (&s)[BN / 16][2], float c,
+                                             const float (&kept)[2], bf16x8 (&pf)[2][BN / 32]) {
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int kb = 0; kb < BN / 16; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = __builtin_fmaf(s[kb][qb][i], c, -kept[qb]);
+        const bool emu = kEmuEvery > 0 && (4 * kb + i) % (kEmuEvery > 0 ? kEmuEvery : 1) == kEmuEvery - 1;
+        pf[qb][kb >> 1][(kb & 1) * 4 + i] = (__bf16)(emu ? exp2_poly(x) : __builtin_amdgcn_exp2f(x));
+      }
 }
 
 // Softmax phase i: first this group's share of the tile loads (below), then
@@ -581,10 +663,10 @@ __device__ __forceinline__ void pp_m_phase(const char* kcur, const char* vprev, 
 // PV(i-1)) the next MFMA phase applies, and P(i).
 template <int BN, int kEmuEvery>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
-                                           const char* vg, int kfill, int vfill, char* kfree,
-                                           char* vcur, float c, const f32x16 (&s)[BN / 32],
-                                           bf16x8 (&pf)[BN / 16], float& alpha, bool& rescale,
-                                           float& kept) {
+                                             const char* vg, int kfill, int vfill, char* kfree,
+                                             char* vcur, float c, const f32x4 (&s)[BN / 16][2],
+                                             bf16x8 (&pf)[2][BN / 32], float (&alpha)[2],
+                                             bool& rescale, float (&kept)[2]) {
   constexpr int kTileBytes = BN * kD * 2;
   // The two groups split the loads so that each phase pair moves one tile:
   // group B fetches K(i+2) into the buffer K(i) left, group A fetches V(i)
@@ -592,23 +674,26 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
   // previous interval). A waits for its loads at the end of this phase;
   // B's are awaited at the end of its next MFMA phase.
   if (group == 1) {
-    if (i + 2 < ntiles) load_tile<BN, kKBlock>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
+    if (i + 2 < ntiles) load_tile<BN, kKBlockPair>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
   } else if (i >= 1) {
     load_tile<BN, kVBlock>(vg + int64_t(i) * kTileBytes, vfill, vcur, wave);
   }
-  alpha = base_update_alpha(tile_max_swap<BN>(s), c, kept);
-  rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-  exp_tile_p<BN, kEmuEvery>(s, c, kept, pf);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) alpha[qb] = base_update_alpha(tile_max16<BN>(s, qb), c, kept[qb]);
+  rescale = __builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0;
+  exp16_tile_p<BN, kEmuEvery>(s, c, kept, pf);
   // P must be complete here, not computed after the barrier where it is
   // first used: the overlap of this phase with the other group's MFMAs
   // depends on it.
 #pragma unroll
-  for (int t = 0; t < BN / 16; ++t) asm volatile("" : "+v"(pf[t]));
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) asm volatile("" : "+v"(pf[qb][t]));
   if (group == 0) wait_vmem();
   barrier();
 }
 
-// Eight-wave variant: two 4-wave groups own two consecutive 128-row Q tiles
+// Eight-wave kernel: two 4-wave groups own two consecutive 128-row Q tiles
 // of one head and share every K/V tile (the article's two-Q-tile CTA,
 // Chapter 5). Barriers make the groups alternate: while one group runs
 // its MFMA phase [PV(i-1), QK(i)] the other runs its softmax phase on the
@@ -629,13 +714,12 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 template <int BN, int kEmuEvery>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
-                              const char* __restrict__ v, __bf16* __restrict__ o,
-                              float* __restrict__ lse, int S, int qtiles, int npairs, int nwg,
-                              float c) {
+                          const char* __restrict__ v, __bf16* __restrict__ o,
+                          float* __restrict__ lse, int S, int qtiles, int npairs, int nwg, float c) {
   static_assert(BN % 64 == 0, "tile shape");
   constexpr int kTileBytes = BN * kD * 2;
   using T = Tiles<BN>;
-  __shared__ uint4 k0[T::kKBytes / 16], k1[T::kKBytes / 16];
+  __shared__ uint4 k0[T::kBlocks * kKBlockPair / 16], k1[T::kBlocks * kKBlockPair / 16];
   __shared__ uint4 v0[T::kVBytes / 16], v1[T::kVBytes / 16];
   char* const kb0 = reinterpret_cast<char*>(k0);
   char* const kb1 = reinterpret_cast<char*>(k1);
@@ -645,10 +729,10 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int group = wave8 >> 2;  // 0 = A, 1 = B
-  const int wave = wave8 & 3;    // wave within the group
-  const int n = lane & 31;
-  const int h = lane >> 5;
+  const int group = wave8 >> 2;
+  const int wave = wave8 & 3;
+  const int col = lane & 15;  // query within a 16-query block
+  const int g = lane >> 4;    // lane group
 
   const int bid = blockIdx.x;
   const int per = nwg >> 3;
@@ -656,8 +740,8 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   const int bh = work / npairs;
   const int pair = work - bh * npairs;
   const int qt_raw = 2 * pair + group;
-  const bool valid = qt_raw < qtiles;       // an odd tile count leaves B's last tile empty
-  const int qt = valid ? qt_raw : qt_raw - 1;  // then B recomputes A's tile and stores nothing
+  const bool valid = qt_raw < qtiles;
+  const int qt = valid ? qt_raw : qt_raw - 1;
   const int64_t head = int64_t(bh) * S * kD;
 
   const char* kg = k + head * 2;
@@ -665,85 +749,91 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   const int ntiles = S / BN;
   const int kfill = k_fill_offset(lane);
   const int vfill = v_fill_offset(lane);
-  const int k_lane = (n >> 2) * kKBlock + ((n & 3) + 4 * h) * 16;
-  const int v_lane = h * kVBlock + 64 * ((lane & 15) >> 2) +
-                     16 * (2 * ((lane >> 4) & 1) + ((lane & 3) >> 1)) + 8 * (lane & 1);
+  // K: row 16kb + col (block 4kb + col/4, row col%4), 16-byte chunk 4*step + g.
+  const int k_lane = (col >> 2) * kKBlockPair + ((col & 3) + 4 * g) * 16;
+  // V: block 8t + g (+4 for the second read), row col/4 of it, d columns
+  // 16db + 4(col%4) .. +3.
+  const int v_lane = g * kVBlock + 64 * (col >> 2) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
 
-  // Prologue loads by all eight waves: K(0), V(0), K(1).
   {
-    // Wave w8 of 8 issues blocks w8, w8+8, ...; reuse the 4-wave loader on
-    // half-tiles.
 #pragma unroll
     for (int i = 0; i < T::kBlocks / 8; ++i) {
       const int j = 8 * i + wave8;
-      __builtin_amdgcn_global_load_lds(kg + j * 1024 + kfill, (lds_void*)(kb0 + j * kKBlock), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(kg + j * 1024 + kfill, (lds_void*)(kb0 + j * kKBlockPair), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vg + j * 1024 + vfill, (lds_void*)(vb0 + j * kVBlock), 16, 0, 0);
       if (ntiles > 1)
         __builtin_amdgcn_global_load_lds(kg + kTileBytes + j * 1024 + kfill,
-                                         (lds_void*)(kb1 + j * kKBlock), 16, 0, 0);
+                                         (lds_void*)(kb1 + j * kKBlockPair), 16, 0, 0);
     }
   }
 
-  const int qrow = qt * kBM + wave * 32 + n;
-  const uint4* qp = q + ((head + int64_t(qrow) * kD) >> 3);
-  bf16x8 qf[8];
+  // Q fragments: query block qb, 32-dim step: dims 32*step + 8g .. +7.
+  const int qrow0 = qt * kBM + wave * 32 + col;  // query of block 0; block 1 is +16
+  bf16x8 qf[2][4];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) qf[kk] = __builtin_bit_cast(bf16x8, qp[2 * kk + h]);
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint4* qp = q + ((head + int64_t(qrow0 + 16 * qb) * kD) >> 3);
+#pragma unroll
+    for (int step = 0; step < 4; ++step) qf[qb][step] = __builtin_bit_cast(bf16x8, qp[4 * step + g]);
+  }
 
-  f32x16 acc[4];
+  f32x4 acc[8][2];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[b][i] = 0.0f;
-  float kept = -FLT_MAX;
-  f32x4 lacc = {0.0f, 0.0f, 0.0f, 0.0f};  // row sum in register 0 (see make_selector)
-  const bf16x8 sel = make_selector(lane);
-  f32x16 s[BN / 32];
-  bf16x8 pf[BN / 16];
+    for (int qb = 0; qb < 2; ++qb) acc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float kept[2] = {-FLT_MAX, -FLT_MAX};
+  f32x4 lacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+  bf16x8 ones;
 #pragma unroll
-  for (int t = 0; t < BN / 16; ++t)
+  for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+  asm volatile("" : "+v"(ones));  // keep it in registers, not rebuilt before each use
+  f32x4 s[BN / 16][2];
+  bf16x8 pf[2][BN / 32];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pf[t][i] = (__bf16)0.0f;
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[qb][t][e] = (__bf16)0.0f;
 
-  __syncthreads();  // prologue tiles are in LDS
-  if (group == 1) barrier();  // phase shift: B starts one interval later
+  __syncthreads();
+  if (group == 1) barrier();
 
-  // M(0) is QK(0) alone; after it every MFMA phase i holds PV(i-1) and
-  // QK(i). K(i) and V(i) live in buffer i % 2. One loop body for all
-  // phases keeps every accumulator in a single set of registers (an
-  // unrolled pair of bodies made the compiler shuttle them between two).
-  qk_only<BN>(kb0, k_lane, qf, s);
+  qk16_tile<BN>(kb0, k_lane, qf, s);
   wait_mem();
   barrier();
-  float alpha;
+  float alpha[2];
   bool rescale;
   pp_v_phase<BN, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha,
                             rescale, kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
-    char* const k_i = odd ? kb1 : kb0;     // K(i), then K(i+2)
-    char* const v_other = odd ? vb0 : vb1;  // V(i-1); group A then loads V(i) into the other buffer
-    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, sel);
+    char* const k_i = odd ? kb1 : kb0;
+    char* const v_other = odd ? vb0 : vb1;
+    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
     if (i == ntiles) break;
     pp_v_phase<BN, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s,
                               pf, alpha, rescale, kept);
   }
-  if (group == 0) barrier();  // matches B's phase-shift barrier
+  if (group == 0) barrier();
 
   if (!valid) return;
-  const float ltot = lacc[0];
-  const float inv = 1.0f / ltot;
-  __bf16* orow = o + head + int64_t(qrow) * kD;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int qb = 0; qb < 2; ++qb) {
+    const float ltot = lacc[qb][0];
+    const float inv = 1.0f / ltot;
+    const int qrow = qrow0 + 16 * qb;
+    __bf16* orow = o + head + int64_t(qrow) * kD;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int db = 0; db < 8; ++db) {
       bf16x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[b][4 * j + i] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * j + 4 * h) = w;
+      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[db][qb][i] * inv);
+      *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g) = w;
     }
-  if (h == 0) lse[int64_t(bh) * S + qrow] = (kept + __log2f(ltot)) * kLn2;
+    if (g == 0) lse[int64_t(bh) * S + qrow] = (kept[qb] + __log2f(ltot)) * kLn2;
+  }
 }
 
 }  // namespace

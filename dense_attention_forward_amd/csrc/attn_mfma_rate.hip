@@ -1,5 +1,6 @@
-// Sustained-rate stream of v_mfma_f32_32x32x16_bf16 (declared in
-// include/attn_mfma_rate.h): four independent accumulators, operands held in
+// Sustained-rate stream of v_mfma_f32_16x16x32_bf16 (declared in
+// include/attn_mfma_rate.h): eight independent accumulators held in VGPRs
+// through tied operands (as the attention kernel holds O), operands in
 // registers, no memory access in the loop.
 #include <hip/hip_runtime.h>
 
@@ -9,7 +10,7 @@
 
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __global__ __launch_bounds__(256) void mfma_rate_kernel(const bf16x8* __restrict__ src,
@@ -21,19 +22,24 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(const bf16x8* __restrict
     a[i] = src[t * 8 + i];
     b[i] = src[t * 8 + 4 + i];
   }
-  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  f32x4 c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[i], c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(i + 1) & 3], b[i], c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[(i + 2) & 3], c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(i + 3) & 3], b[(i + 1) & 3], c3, 0, 0, 0);
-    }
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0"
+                     : "+v"(c[i])
+                     : "v"(a[(i + r) & 3]), "v"(b[(i + 2 * r) & 3]));
   }
+  // the results are read next by VALU code: wait out the MFMA write-back
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]),
+               "+v"(c[5]), "+v"(c[6]), "+v"(c[7]));
   float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  for (int i = 0; i < 8; ++i) s += c[i][0] + c[i][1] + c[i][2] + c[i][3];
   sink[t] = s;
 }
 

@@ -1,8 +1,8 @@
 /*
  * attn_mfma_rate.h -- measurement helper shipped with the attention library:
  * the sustained rate of the matrix cores on this GPU for the instruction the
- * attention kernels spend their time in (v_mfma_f32_32x32x16_bf16), on
- * operands the caller chooses.
+ * eight-wave attention kernel spends its time in (v_mfma_f32_16x16x32_bf16),
+ * on operands the caller chooses.
  *
  * Why: the published dense bf16 peak assumes the top clock, but under a
  * sustained MFMA load the clock is set by power, and power depends on how
@@ -13,10 +13,11 @@
  * attn_mfma_rate enqueues one kernel of `workgroups` workgroups of 256
  * threads (4 waves). Every thread reads 128 bytes of bf16 operands from
  * `operands` (thread t at byte offset 128 * t: four A and four B
- * fragments) and then issues `iters` rounds of 16 MFMAs (four independent
- * accumulators) from registers, with no memory access in the loop; it
- * finally writes one float per thread to `sink` so that nothing is
- * optimised away. FLOPs per launch = workgroups * 4 * iters * 16 * 32768.
+ * fragments) and then issues `iters` rounds of 32 MFMAs (eight independent
+ * accumulators in VGPRs, as in the attention kernel) from registers, with
+ * no memory access in the loop; it finally writes one float per thread to
+ * `sink` so that nothing is optimised away. FLOPs per launch =
+ * workgroups * 4 * iters * 32 * 16384.
  *
  *   operands : device, 16-byte aligned, workgroups * 256 * 128 bytes, read only
  *   sink     : device float32, workgroups * 256 elements, written
