@@ -639,23 +639,22 @@ __device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][2], int qb
   return max_over_groups(__builtin_elementwise_maximum(m0, m1));
 }
 
-// P = 2^(s*c - kept) in bf16 as PV B operands: step t of query block qb
-// takes slots 0..3 from score block 2t and slots 4..7 from block 2t+1.
-// kEmuEvery = 0: every exponential on v_exp_f32. kEmuEvery = k: one element
-// in k (those with (4 kb + i) % k == k - 1) takes exp2_poly instead.
-template <int BN, int kEmuEvery>
-__device__ __forceinline__ void exp16_tile_p(const f32x4 (&s)[BN / 16][2], float c,
-                                             const float (&kept)[2], bf16x8 (&pf)[2][BN / 32]) {
+// P = 2^(s*c - kept) in bf16 as PV B operands, for score blocks kb0 .. kb1-1
+// of query block qb: step t takes slots 0..3 from score block 2t and slots
+// 4..7 from block 2t+1. kEmuEvery = 0: every exponential on v_exp_f32.
+// kEmuEvery = k: one element in k (those with (4 kb + i) % k == k - 1) takes
+// exp2_poly instead.
+template <int BN, int kEmuEvery, int qb, int kb0, int kb1>
+__device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][2], float c, const float (&kept)[2],
+                                           bf16x8 (&pf)[2][BN / 32]) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int kb = kb0; kb < kb1; ++kb)
 #pragma unroll
-    for (int kb = 0; kb < BN / 16; ++kb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = __builtin_fmaf(s[kb][qb][i], c, -kept[qb]);
-        const bool emu = kEmuEvery > 0 && (4 * kb + i) % (kEmuEvery > 0 ? kEmuEvery : 1) == kEmuEvery - 1;
-        pf[qb][kb >> 1][(kb & 1) * 4 + i] = (__bf16)(emu ? exp2_poly(x) : __builtin_amdgcn_exp2f(x));
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float x = __builtin_fmaf(s[kb][qb][i], c, -kept[qb]);
+      const bool emu = kEmuEvery > 0 && (4 * kb + i) % (kEmuEvery > 0 ? kEmuEvery : 1) == kEmuEvery - 1;
+      pf[qb][kb >> 1][(kb & 1) * 4 + i] = (__bf16)(emu ? exp2_poly(x) : __builtin_amdgcn_exp2f(x));
+    }
 }
 
 // Softmax phase i: first this group's share of the tile loads (below), then
@@ -668,20 +667,47 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
                                              bf16x8 (&pf)[2][BN / 32], float (&alpha)[2],
                                              bool& rescale, float (&kept)[2]) {
   constexpr int kTileBytes = BN * kD * 2;
+  static_assert(Tiles<BN>::kLoadsPerWave == 8 && BN / 16 == 8, "load spread assumes 128-key tiles");
   // The two groups split the loads so that each phase pair moves one tile:
   // group B fetches K(i+2) into the buffer K(i) left, group A fetches V(i)
   // into the buffer V(i-2) left (both buffers' last readers finished in the
   // previous interval). A waits for its loads at the end of this phase;
   // B's are awaited at the end of its next MFMA phase.
-  if (group == 1) {
-    if (i + 2 < ntiles) load_tile<BN, kKBlockPair>(kg + int64_t(i + 2) * kTileBytes, kfill, kfree, wave);
-  } else if (i >= 1) {
-    load_tile<BN, kVBlock>(vg + int64_t(i) * kTileBytes, vfill, vcur, wave);
-  }
+  //
+  // The 4 waves of a group move 32 KB per phase through the CU's vector
+  // memory path, and a wave's load issue stalls while that path is busy.
+  // The wave's 8 loads are therefore spread over the phase, two at a time
+  // between parts of the softmax work, instead of being issued up front.
+  const bool kside = group == 1;
+  const bool load = kside ? i + 2 < ntiles : i >= 1;
+  const char* src = kside ? kg + int64_t(i + 2) * kTileBytes : vg + int64_t(i) * kTileBytes;
+  char* const dst = kside ? kfree : vcur;
+  const int fill = kside ? kfill : vfill;
+  const int stride = kside ? kKBlockPair : kVBlock;
+  auto issue2 = [&](int ii) {
+    if (load) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const int j = 4 * (ii + x) + wave;
+        __builtin_amdgcn_global_load_lds(src + j * 1024 + fill, (lds_void*)(dst + j * stride), 16, 0, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue2(0);
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) alpha[qb] = base_update_alpha(tile_max16<BN>(s, qb), c, kept[qb]);
   rescale = __builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0;
-  exp16_tile_p<BN, kEmuEvery>(s, c, kept, pf);
+  issue2(2);
+  // The empty assembly statements pin each part of P before the next loads
+  // (the compiler would otherwise sink all exponentials below them).
+  exp16_part<BN, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
+  asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
+  issue2(4);
+  exp16_part<BN, kEmuEvery, 1, 0, 4>(s, c, kept, pf);
+  asm volatile("" : "+v"(pf[1][0]), "+v"(pf[1][1]));
+  issue2(6);
+  exp16_part<BN, kEmuEvery, 1, 4, 8>(s, c, kept, pf);
   // P must be complete here, not computed after the barrier where it is
   // first used: the overlap of this phase with the other group's MFMAs
   // depends on it.
