@@ -58,7 +58,11 @@ def measured_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def time_workload(daf, torch, w, steps: int, warmup: int):
+def time_workload(daf, torch, w, steps: int, warmup: int, min_warm_s: float = 0.0):
+    """Times `steps` launches after `warmup` untimed ones (and, with
+    min_warm_s, more untimed ones until that much wall time has passed: the
+    GPU idles while the inputs are drawn on the host, and its clock takes a
+    while to come back up)."""
     dev = torch.device("cuda", 0)
     q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
     o = torch.empty_like(q)
@@ -66,6 +70,11 @@ def time_workload(daf, torch, w, steps: int, warmup: int):
     for _ in range(warmup):
         daf.forward(q, k, v, w.scale, out=o, lse=lse)
     torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < min_warm_s:
+        for _ in range(10):
+            daf.forward(q, k, v, w.scale, out=o, lse=lse)
+        torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)  # the kernels are enqueued on this stream
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -191,7 +200,7 @@ def main() -> int:
                 per[name] = {"tflops": round(tflops, 1), "ms": round(ms, 4)}
                 continue
             wx = workloads.get(name)
-            msx, _, okx = time_workload(daf, torch, wx, max(5, args.steps), 3)
+            msx, _, okx = time_workload(daf, torch, wx, max(5, args.steps), 3, min_warm_s=0.3)
             ok = ok and okx
             per[name] = {"tflops": round(wx.flops / (msx * 1e-3) / 1e12, 1), "ms": round(msx, 4)}
 

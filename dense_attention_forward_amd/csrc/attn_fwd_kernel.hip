@@ -877,27 +877,42 @@ int pick_variant(int B, int H, int S) {
   return pair_wgs >= ATTN_PP_MIN_WGS ? ATTN_VARIANT_PAIR256 : ATTN_VARIANT_TILE128;
 }
 
+namespace {
+template <class T>
+struct same_type {
+  using type = T;
+};
+// hipLaunchKernel with the kernel's own parameter types: returns the status
+// of this launch (not an error left behind by earlier runtime calls, as
+// hipGetLastError after the <<<>>> form would).
+template <typename... KArgs>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         typename same_type<KArgs>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, 0, stream);
+}
+}  // namespace
+
 hipError_t launch(const Params& p, hipStream_t stream) {
   constexpr int BN = ATTN_BN;
   const int qtiles = p.S / kBM;
   const float c = p.scale * kLog2e;
+  const auto* q = static_cast<const uint4*>(p.q);
+  const auto* k = static_cast<const char*>(p.k);
+  const auto* v = static_cast<const char*>(p.v);
+  auto* o = static_cast<__bf16*>(p.o);
   if (p.variant == ATTN_VARIANT_PAIR256 || p.variant == ATTN_VARIANT_PAIR256_EXP2EMU) {
     const int npairs = (qtiles + 1) / 2;
     const int nwg = int(int64_t(p.B) * p.H * npairs);
     // PAIR256_EXP2EMU: one exponential in four on the FMA pipe
     auto kernel = p.variant == ATTN_VARIANT_PAIR256 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 0>
                                                     : attn_fwd_pingpong_kernel<ATTN_PP_BN, 4>;
-    hipLaunchKernelGGL(kernel, dim3(nwg), dim3(2 * kThreads), 0, stream, static_cast<const uint4*>(p.q),
-                       static_cast<const char*>(p.k), static_cast<const char*>(p.v),
-                       static_cast<__bf16*>(p.o), p.lse, p.S, qtiles, npairs, nwg, c);
-    return hipGetLastError();
+    return launch_kernel(kernel, dim3(nwg), dim3(2 * kThreads), stream, q, k, v, o, p.lse, p.S, qtiles,
+                         npairs, nwg, c);
   }
   const int nwg = p.B * p.H * qtiles;
-  hipLaunchKernelGGL(attn_fwd_kernel<BN>, dim3(nwg), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(p.q), static_cast<const char*>(p.k),
-                     static_cast<const char*>(p.v), static_cast<__bf16*>(p.o), p.lse, p.S,
-                     qtiles, nwg, c);
-  return hipGetLastError();
+  return launch_kernel(attn_fwd_kernel<BN>, dim3(nwg), dim3(kThreads), stream, q, k, v, o, p.lse, p.S,
+                       qtiles, nwg, c);
 }
 
 }  // namespace attn_detail

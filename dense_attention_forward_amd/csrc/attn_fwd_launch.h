@@ -15,7 +15,7 @@ struct Params {
   float* lse;
   int B, H, S;
   float scale;
-  int variant;  // ATTN_VARIANT_TILE128 or ATTN_VARIANT_PAIR256 (resolved, never AUTO)
+  int variant;  // TILE128, PAIR256 or PAIR256_EXP2EMU (resolved, never AUTO)
 };
 
 // The variant chosen for a shape when the caller leaves it to the library.
