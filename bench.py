@@ -154,7 +154,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=HEADLINE, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
