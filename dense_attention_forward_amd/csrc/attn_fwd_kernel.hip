@@ -487,7 +487,8 @@ struct MmaRing {
 //  * The row sum is a 16x16x32 MFMA of an all-ones A with the same P
 //    operand: every row of its D is the key sum of lane l's query.
 //  * Every K and V fragment read from LDS feeds the MFMAs of both query
-//    blocks, so LDS traffic per FLOP is that of the 32x32x16 kernel.
+//    blocks, so LDS traffic per FLOP is that of the four-wave kernel's
+//    32x32x16 MFMAs (one fragment per 32x32 output block).
 // ---------------------------------------------------------------------------
 
 // Fragments of an MFMA phase in issue order: first the V fragments of
@@ -532,7 +533,9 @@ __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsign
     constexpr int db = F % 8, t = F / 8;
     lgkm_wait<N>();
     const u32x4 a = __builtin_shufflevector(ring.vlo[slot], ring.vhi[slot], 0, 1, 2, 3);
-    // In place through tied operands, as in the 32x32x16 kernel.
+    // In place through tied operands: each O accumulator keeps one register
+    // set (with the builtin the allocator moved the accumulators between
+    // two sets every phase).
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][0]) : "v"(a), "v"(pf[0][t]));
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][1]) : "v"(a), "v"(pf[1][t]));
     if constexpr (db == 7) {
