@@ -19,7 +19,7 @@ STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL", 2: "ATTN_ERR_SHAPE", 3: "ATTN_ERR_ALIGN",
     4: "ATTN_ERR_SCALE", 5: "ATTN_ERR_OVERLAP", 6: "ATTN_ERR_LAUNCH", 7: "ATTN_ERR_VARIANT",
 }
-VARIANT_AUTO, VARIANT_TILE128, VARIANT_PAIR256, VARIANT_PAIR256_EXP2EMU = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_TILE128, VARIANT_PAIR256, VARIANT_PAIR256_EXP2EMU, VARIANT_PAIR128 = 0, 1, 2, 3, 4
 HEAD_DIM = 128
 
 _lock = threading.Lock()

@@ -49,7 +49,8 @@ extern "C" int attn_fwd_pick(int B, int H, int S) { return attn_detail::pick_var
 extern "C" int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int S, int D, float scale, int variant, void* stream) {
   if (variant != ATTN_VARIANT_AUTO && variant != ATTN_VARIANT_TILE128 &&
-      variant != ATTN_VARIANT_PAIR256 && variant != ATTN_VARIANT_PAIR256_EXP2EMU)
+      variant != ATTN_VARIANT_PAIR256 && variant != ATTN_VARIANT_PAIR256_EXP2EMU &&
+      variant != ATTN_VARIANT_PAIR128)
     return ATTN_ERR_VARIANT;
   const int status = attn_fwd_check(q, k, v, o, lse, B, H, S, D, scale);
   if (status != ATTN_OK) return status;

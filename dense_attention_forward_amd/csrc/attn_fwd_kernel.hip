@@ -522,11 +522,11 @@ __device__ __forceinline__ void issue_frag16(MmaRing& ring, unsigned kaddr, unsi
   }
 }
 
-template <int BN, int F>
+template <int BN, int QB, int F>
 __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsigned vaddr,
-                                           const bf16x8 (&qf)[2][4], f32x4 (&s)[BN / 16][2],
-                                           const bf16x8 (&pf)[2][BN / 32], f32x4 (&acc)[8][2],
-                                           f32x4 (&lacc)[2], const bf16x8& ones) {
+                                           const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
+                                           const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
+                                           f32x4 (&lacc)[QB], const bf16x8& ones) {
   constexpr int slot = F % ATTN_PREFETCH;
   constexpr int N = Frags16<BN>::after(F, ATTN_PREFETCH);
   if constexpr (F < Frags16<BN>::kV) {
@@ -537,13 +537,14 @@ __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsign
     // set (with the builtin the allocator moved the accumulators between
     // two sets every phase).
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][0]) : "v"(a), "v"(pf[0][t]));
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][1]) : "v"(a), "v"(pf[1][t]));
+    if constexpr (QB == 2)
+      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][QB - 1]) : "v"(a), "v"(pf[QB - 1][t]));
     if constexpr (db == 7) {
       // Row sums of step t's P, the same rounded values the PV used. As
       // builtins, so that the compiler's hazard checks cover any copy it
       // makes of the operands.
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
         lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][t], lacc[qb], 0, 0, 0);
     }
   } else {
@@ -553,14 +554,14 @@ __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsign
     const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
     const f32x4 zero = {};
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < QB; ++qb)
       s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
                                                           0, 0, 0);
   }
   if constexpr (F + ATTN_PREFETCH < Frags16<BN>::kTotal) issue_frag16<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (F + 1 < Frags16<BN>::kTotal)
-    mma_step16<BN, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
+    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
 }
 
 template <int BN, int F>
@@ -573,39 +574,39 @@ __device__ __forceinline__ void issue_first16(MmaRing& ring, unsigned kaddr, uns
 // some row of the wave rebased), PV(i-1) and QK(i), then publish this
 // wave's finished loads and pass a barrier. The epilogue and the next
 // rescale read O long after its last MFMA (the QK steps follow it).
-template <int BN>
+template <int BN, int QB>
 __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
-                                             const bf16x8 (&qf)[2][4], f32x4 (&s)[BN / 16][2],
-                                             const bf16x8 (&pf)[2][BN / 32], f32x4 (&acc)[8][2],
-                                             const float (&alpha)[2], bool rescale, f32x4 (&lacc)[2],
+                                             const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
+                                             const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
+                                             const float (&alpha)[QB], bool rescale, f32x4 (&lacc)[QB],
                                              const bf16x8& ones) {
   if (rescale) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) acc[db][qb] *= alpha[qb];
       lacc[qb] *= alpha[qb];
     }
     // The PV MFMAs below are inline assembly, which the compiler's hazard
     // checks do not see: give the VALU writes their wait states here.
-    asm volatile("s_nop 4" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]),
-                 "+v"(acc[2][0]), "+v"(acc[2][1]), "+v"(acc[3][0]), "+v"(acc[3][1]), "+v"(acc[4][0]),
-                 "+v"(acc[4][1]), "+v"(acc[5][0]), "+v"(acc[5][1]), "+v"(acc[6][0]), "+v"(acc[6][1]),
-                 "+v"(acc[7][0]), "+v"(acc[7][1]), "+v"(lacc[0]), "+v"(lacc[1]));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      asm volatile("s_nop 4" : "+v"(acc[0][qb]), "+v"(acc[1][qb]), "+v"(acc[2][qb]), "+v"(acc[3][qb]),
+                   "+v"(acc[4][qb]), "+v"(acc[5][qb]), "+v"(acc[6][qb]), "+v"(acc[7][qb]), "+v"(lacc[qb]));
   }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing ring;
   issue_first16<BN, 0>(ring, kaddr, vaddr);
-  mma_step16<BN, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
+  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
   wait_mem();
   barrier();
 }
 
 // QK of the first K tile alone, with plain builtins.
-template <int BN>
-__device__ __forceinline__ void qk16_tile(const char* ksm, int k_lane, const bf16x8 (&qf)[2][4],
-                                          f32x4 (&s)[BN / 16][2]) {
+template <int BN, int QB>
+__device__ __forceinline__ void qk16_tile(const char* ksm, int k_lane, const bf16x8 (&qf)[QB][4],
+                                          f32x4 (&s)[BN / 16][QB]) {
 #pragma unroll
   for (int kb = 0; kb < BN / 16; ++kb)
 #pragma unroll
@@ -614,7 +615,7 @@ __device__ __forceinline__ void qk16_tile(const char* ksm, int k_lane, const bf1
           *reinterpret_cast<const bf16x8*>(ksm + k_lane + kb * 4 * kKBlockPair + step * 256);
       const f32x4 zero = {};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
         s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
                                                             0, 0, 0);
     }
@@ -630,8 +631,8 @@ __device__ __forceinline__ float max_over_groups(float x) {
 
 // Raw row max of query block qb over the tile: two v_maximum3 chains over
 // the lane's 4 * BN/16 scores, then the exchange between lane groups.
-template <int BN>
-__device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][2], int qb) {
+template <int BN, int QB>
+__device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][QB], int qb) {
   float m0 = __builtin_elementwise_maximum(s[0][qb][0], s[0][qb][1]);
   float m1 = __builtin_elementwise_maximum(s[0][qb][2], s[0][qb][3]);
 #pragma unroll
@@ -647,9 +648,9 @@ __device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][2], int qb
 // 4..7 from block 2t+1. kEmuEvery = 0: every exponential on v_exp_f32.
 // kEmuEvery = k: one element in k (those with (4 kb + i) % k == k - 1) takes
 // exp2_poly instead.
-template <int BN, int kEmuEvery, int qb, int kb0, int kb1>
-__device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][2], float c, const float (&kept)[2],
-                                           bf16x8 (&pf)[2][BN / 32]) {
+template <int BN, int QB, int kEmuEvery, int qb, int kb0, int kb1>
+__device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float c, const float (&kept)[QB],
+                                           bf16x8 (&pf)[QB][BN / 32]) {
 #pragma unroll
   for (int kb = kb0; kb < kb1; ++kb)
 #pragma unroll
@@ -663,12 +664,12 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][2], float c
 // Softmax phase i: first this group's share of the tile loads (below), then
 // the row max and base update, whose factor for O (already holding
 // PV(i-1)) the next MFMA phase applies, and P(i).
-template <int BN, int kEmuEvery>
+template <int BN, int QB, int kEmuEvery>
 __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
                                              const char* vg, int kfill, int vfill, char* kfree,
-                                             char* vcur, float c, const f32x4 (&s)[BN / 16][2],
-                                             bf16x8 (&pf)[2][BN / 32], float (&alpha)[2],
-                                             bool& rescale, float (&kept)[2]) {
+                                             char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
+                                             bf16x8 (&pf)[QB][BN / 32], float (&alpha)[QB],
+                                             bool& rescale, float (&kept)[QB]) {
   constexpr int kTileBytes = BN * kD * 2;
   static_assert(Tiles<BN>::kLoadsPerWave == 8 && BN / 16 == 8, "load spread assumes 128-key tiles");
   // The two groups split the loads so that each phase pair moves one tile:
@@ -699,23 +700,36 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
   };
   issue2(0);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) alpha[qb] = base_update_alpha(tile_max16<BN>(s, qb), c, kept[qb]);
-  rescale = __builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0;
+  for (int qb = 0; qb < QB; ++qb) alpha[qb] = base_update_alpha(tile_max16<BN, QB>(s, qb), c, kept[qb]);
+  bool rebased = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) rebased = rebased || alpha[qb] != 1.0f;
+  rescale = __builtin_amdgcn_ballot_w64(rebased) != 0;
   issue2(2);
   // The empty assembly statements pin each part of P before the next loads
   // (the compiler would otherwise sink all exponentials below them).
-  exp16_part<BN, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
-  asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
-  issue2(4);
-  exp16_part<BN, kEmuEvery, 1, 0, 4>(s, c, kept, pf);
-  asm volatile("" : "+v"(pf[1][0]), "+v"(pf[1][1]));
-  issue2(6);
-  exp16_part<BN, kEmuEvery, 1, 4, 8>(s, c, kept, pf);
+  if constexpr (QB == 2) {
+    exp16_part<BN, QB, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
+    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
+    issue2(4);
+    exp16_part<BN, QB, kEmuEvery, QB - 1, 0, 4>(s, c, kept, pf);
+    asm volatile("" : "+v"(pf[QB - 1][0]), "+v"(pf[QB - 1][1]));
+    issue2(6);
+    exp16_part<BN, QB, kEmuEvery, QB - 1, 4, 8>(s, c, kept, pf);
+  } else {
+    exp16_part<BN, QB, kEmuEvery, 0, 0, 4>(s, c, kept, pf);
+    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]));
+    issue2(4);
+    exp16_part<BN, QB, kEmuEvery, 0, 4, 6>(s, c, kept, pf);
+    asm volatile("" : "+v"(pf[0][2]));
+    issue2(6);
+    exp16_part<BN, QB, kEmuEvery, 0, 6, 8>(s, c, kept, pf);
+  }
   // P must be complete here, not computed after the barrier where it is
   // first used: the overlap of this phase with the other group's MFMAs
   // depends on it.
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) asm volatile("" : "+v"(pf[qb][t]));
   if (group == 0) wait_vmem();
@@ -740,7 +754,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 // The MFMA phase also takes the row sum of the P it consumes, on the matrix
 // pipe; the softmax phase keeps the row max, the base update and the
 // exponentials.
-template <int BN, int kEmuEvery>
+template <int BN, int QB, int kEmuEvery>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
                           const char* __restrict__ v, __bf16* __restrict__ o,
@@ -797,30 +811,35 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   }
 
   // Q fragments: query block qb, 32-dim step: dims 32*step + 8g .. +7.
-  const int qrow0 = qt * kBM + wave * 32 + col;  // query of block 0; block 1 is +16
-  bf16x8 qf[2][4];
+  const int qrow0 = qt * (64 * QB) + wave * (16 * QB) + col;  // query of block 0; block qb is +16 qb
+  bf16x8 qf[QB][4];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const uint4* qp = q + ((head + int64_t(qrow0 + 16 * qb) * kD) >> 3);
 #pragma unroll
     for (int step = 0; step < 4; ++step) qf[qb][step] = __builtin_bit_cast(bf16x8, qp[4 * step + g]);
   }
 
-  f32x4 acc[8][2];
+  f32x4 acc[8][QB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) acc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float kept[2] = {-FLT_MAX, -FLT_MAX};
-  f32x4 lacc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float kept[QB];
+  f32x4 lacc[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    kept[qb] = -FLT_MAX;
+    lacc[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   asm volatile("" : "+v"(ones));  // keep it in registers, not rebuilt before each use
-  f32x4 s[BN / 16][2];
-  bf16x8 pf[2][BN / 32];
+  f32x4 s[BN / 16][QB];
+  bf16x8 pf[QB][BN / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t)
 #pragma unroll
@@ -829,27 +848,27 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   __syncthreads();
   if (group == 1) barrier();
 
-  qk16_tile<BN>(kb0, k_lane, qf, s);
+  qk16_tile<BN, QB>(kb0, k_lane, qf, s);
   wait_mem();
   barrier();
-  float alpha[2];
+  float alpha[QB];
   bool rescale;
-  pp_v_phase<BN, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha,
+  pp_v_phase<BN, QB, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha,
                             rescale, kept);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
-    pp_m_phase<BN>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
     if (i == ntiles) break;
-    pp_v_phase<BN, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s,
+    pp_v_phase<BN, QB, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s,
                               pf, alpha, rescale, kept);
   }
   if (group == 0) barrier();
 
   if (!valid) return;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float ltot = lacc[qb][0];
     const float inv = 1.0f / ltot;
     const int qrow = qrow0 + 16 * qb;
@@ -871,13 +890,22 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #define ATTN_PP_BN 128
 #endif
 #ifndef ATTN_PP_MIN_WGS
-#define ATTN_PP_MIN_WGS 512
+#define ATTN_PP_MIN_WGS 256
 #endif
 
 
+// PAIR256 once its workgroups (pairs of 128-row tiles) fill the GPU's CUs
+// once; below that PAIR128 (pairs of 64-row tiles), down to launches of a
+// handful of workgroups, which one 128-row tile per workgroup serves a little
+// faster. Measured: from 256 PAIR256 workgroups up PAIR256 is fastest; below,
+// PAIR128 beats TILE128 by 13-48% at 32-256 workgroups; at 2 workgroups
+// (S = 256, one head) TILE128 is 5% ahead.
 int pick_variant(int B, int H, int S) {
   const int64_t pair_wgs = int64_t(B) * H * ((S / kBM + 1) / 2);
-  return pair_wgs >= ATTN_PP_MIN_WGS ? ATTN_VARIANT_PAIR256 : ATTN_VARIANT_TILE128;
+  const int64_t half_pair_wgs = int64_t(B) * H * (S / (2 * 64));
+  if (pair_wgs >= ATTN_PP_MIN_WGS) return ATTN_VARIANT_PAIR256;
+  if (half_pair_wgs >= 16) return ATTN_VARIANT_PAIR128;
+  return ATTN_VARIANT_TILE128;
 }
 
 namespace {
@@ -904,13 +932,20 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const auto* k = static_cast<const char*>(p.k);
   const auto* v = static_cast<const char*>(p.v);
   auto* o = static_cast<__bf16*>(p.o);
-  if (p.variant == ATTN_VARIANT_PAIR256 || p.variant == ATTN_VARIANT_PAIR256_EXP2EMU) {
-    const int npairs = (qtiles + 1) / 2;
+  if (p.variant == ATTN_VARIANT_PAIR256 || p.variant == ATTN_VARIANT_PAIR256_EXP2EMU ||
+      p.variant == ATTN_VARIANT_PAIR128) {
+    // PAIR256: two 128-row query tiles per workgroup (two 16-query blocks
+    // per wave); PAIR128: two 64-row tiles (one block per wave), for grids
+    // too small to fill the GPU with 256-row workgroups.
+    const int rows = p.variant == ATTN_VARIANT_PAIR128 ? 64 : 128;
+    const int tiles = p.S / rows;
+    const int npairs = (tiles + 1) / 2;
     const int nwg = int(int64_t(p.B) * p.H * npairs);
     // PAIR256_EXP2EMU: one exponential in four on the FMA pipe
-    auto kernel = p.variant == ATTN_VARIANT_PAIR256 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 0>
-                                                    : attn_fwd_pingpong_kernel<ATTN_PP_BN, 4>;
-    return launch_kernel(kernel, dim3(nwg), dim3(2 * kThreads), stream, q, k, v, o, p.lse, p.S, qtiles,
+    auto kernel = p.variant == ATTN_VARIANT_PAIR256   ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, 0>
+                  : p.variant == ATTN_VARIANT_PAIR128 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 1, 0>
+                                                      : attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, 4>;
+    return launch_kernel(kernel, dim3(nwg), dim3(2 * kThreads), stream, q, k, v, o, p.lse, p.S, tiles,
                          npairs, nwg, c);
   }
   const int nwg = p.B * p.H * qtiles;

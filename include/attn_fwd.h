@@ -64,12 +64,15 @@ enum attn_status {
  *                          of the exponent unit (the article's Chapter 9
  *                          "software approximations"); for measurement,
  *                          never picked by attn_fwd
+ *   ATTN_VARIANT_PAIR128 : PAIR256's 8-wave workgroups with two 64-row
+ *                          query tiles, for mid-sized grids
  */
 enum attn_variant {
   ATTN_VARIANT_AUTO = 0,
   ATTN_VARIANT_TILE128 = 1,
   ATTN_VARIANT_PAIR256 = 2,
-  ATTN_VARIANT_PAIR256_EXP2EMU = 3
+  ATTN_VARIANT_PAIR256_EXP2EMU = 3,
+  ATTN_VARIANT_PAIR128 = 4
 };
 
 /*
@@ -96,9 +99,10 @@ int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float
                      int B, int H, int S, int D, float scale, int variant, void* stream);
 
 /*
- * The variant attn_fwd picks for a shape (pure host code): PAIR256 when the
- * grid of query-tile pairs is large enough to fill the GPU, else TILE128.
- * Returns ATTN_VARIANT_TILE128 or ATTN_VARIANT_PAIR256.
+ * The variant attn_fwd picks for a shape (pure host code): PAIR256 when its
+ * grid of 128-row tile pairs has at least 256 workgroups, else PAIR128 when
+ * its grid of 64-row tile pairs has at least 16, else TILE128.
+ * Returns ATTN_VARIANT_TILE128, ATTN_VARIANT_PAIR128 or ATTN_VARIANT_PAIR256.
  */
 int attn_fwd_pick(int B, int H, int S);
 

@@ -133,16 +133,25 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
 
 
 def test_variant_rejected_before_launch(lib):
-    for bad in (-1, 4, 99):
+    for bad in (-1, 5, 99):
         assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, D, SC, 0, variant=bad) == 7
     # a valid variant with bad arguments still reports the argument error
     assert lib.attn_fwd_raw(Q, K, V, O, L, B, H, S, 64, SC, 0, variant=2) == 2
 
 
 def test_pick(lib):
-    # small grids of query-tile pairs keep one 128-row tile per workgroup
+    # launches of a few workgroups keep one 128-row tile per workgroup
     assert lib.pick(1, 1, 256) == lib.VARIANT_TILE128
-    assert lib.pick(2, 16, 1024) == lib.VARIANT_TILE128
+    assert lib.pick(1, 1, 1024) == lib.VARIANT_TILE128
+    # below a full round of 256-row workgroups: pairs of 64-row tiles
+    assert lib.pick(1, 4, 1024) == lib.VARIANT_PAIR128
+    assert lib.pick(1, 1, 8192) == lib.VARIANT_PAIR128
+    assert lib.pick(2, 16, 1024) == lib.VARIANT_PAIR128
+    assert lib.pick(1, 16, 2048) == lib.VARIANT_PAIR128
+    assert lib.pick(2, 8, 1024) == lib.VARIANT_PAIR128
+    # one full round of 256-row workgroups and more
+    assert lib.pick(2, 16, 2048) == lib.VARIANT_PAIR256
+    assert lib.pick(4, 16, 1024) == lib.VARIANT_PAIR256
     # the 4K/8K/16K workloads fill the GPU with tile pairs
     assert lib.pick(4, 16, 4096) == lib.VARIANT_PAIR256
     assert lib.pick(2, 16, 8192) == lib.VARIANT_PAIR256

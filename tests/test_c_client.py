@@ -47,7 +47,7 @@ def test_c_client_host_checks(tmp_path):
 @pytest.mark.gpu
 @pytest.mark.parametrize("B,H,S", [(1, 2, 384), (1, 32, 4096)])
 def test_c_client_runs_attention(tmp_path, B, H, S):
-    """S = 384 takes the four-wave kernel, S = 4096 at H = 32 (512 tile pairs) the eight-wave one."""
+    """S = 384 at H = 2 takes the four-wave kernel, S = 4096 at H = 32 the eight-wave PAIR256."""
     print(f"case C client B={B} H={H} S={S}", flush=True)
     exe = _compile(tmp_path)
     q, k, v = make_random(B, H, S, 128, seed=31)

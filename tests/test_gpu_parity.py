@@ -36,7 +36,7 @@ def _say(msg):
     sys.stdout.flush()
 
 
-VARIANTS = [1, 2, 3]  # TILE128, PAIR256, PAIR256_EXP2EMU (forced, whatever attn_fwd would pick)
+VARIANTS = [1, 2, 3, 4]  # TILE128, PAIR256, PAIR256_EXP2EMU, PAIR128 (forced, whatever attn_fwd would pick)
 
 
 def _run(daf, q, k, v, scale=DEFAULT_SCALE, variant=0):

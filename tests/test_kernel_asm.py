@@ -91,4 +91,4 @@ def test_eight_wave_kernels_do_not_spill(tmp_path):
         assert re.search(r"\.vgpr_spill_count:\s+0\b", body), name
         assert re.search(r"\.private_segment_fixed_size:\s+0\b", body), name
         checked += 1
-    assert checked == 2
+    assert checked == 3
