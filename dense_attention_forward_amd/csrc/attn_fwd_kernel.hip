@@ -465,7 +465,7 @@ struct MmaRing {
 };
 
 // ---------------------------------------------------------------------------
-// Eight-wave kernel (variants PAIR256, PAIR256_EXP2EMU) on
+// Eight-wave kernel (variants PAIR256, PAIR256_EXP2EMU, PAIR128) on
 // v_mfma_f32_16x16x32_bf16. Same LDS layouts and tile loads as the four-wave
 // kernel; a stream of 16x16x32 MFMAs sustains a markedly higher rate on
 // gfx950 than one of 32x32x16 MFMAs, though both do 1024 FLOPs per cycle
@@ -474,7 +474,9 @@ struct MmaRing {
 //
 // D[16x16] += A[16x32] . B[32x16]: lane l holds row l%16 of A and column
 // l%16 of B, each with k = 8g .. 8g+7 where g = l/16, and column l%16 of D
-// at rows 4g .. 4g+3. Each wave owns 32 queries as two 16-query blocks qb.
+// at rows 4g .. 4g+3. Each wave owns QB 16-query blocks qb: QB = 2 (32
+// queries, 128-row tiles per group; PAIR256) or QB = 1 (16 queries, 64-row
+// tiles; PAIR128, for grids too small to fill the GPU otherwise).
 //  * S^T = K . Q^T per 16-key block kb: A = K rows (keys) from LDS, B = Q
 //    (registers). Lane l then holds query 16qb + l%16, keys 16kb + 4g + i.
 //    A query's scores are spread over the four lane groups g, so the row
@@ -486,9 +488,10 @@ struct MmaRing {
 //    gathered for those keys with two ds_read_b64_tr_b16 per fragment.
 //  * The row sum is a 16x16x32 MFMA of an all-ones A with the same P
 //    operand: every row of its D is the key sum of lane l's query.
-//  * Every K and V fragment read from LDS feeds the MFMAs of both query
-//    blocks, so LDS traffic per FLOP is that of the four-wave kernel's
-//    32x32x16 MFMAs (one fragment per 32x32 output block).
+//  * With QB = 2 every K and V fragment read from LDS feeds the MFMAs of
+//    both query blocks, so LDS traffic per FLOP is that of the four-wave
+//    kernel's 32x32x16 MFMAs (one fragment per 32x32 output block). With
+//    QB = 1 it doubles, and the PV steps wait on the LDS.
 // ---------------------------------------------------------------------------
 
 // Fragments of an MFMA phase in issue order: first the V fragments of
