@@ -104,6 +104,8 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None, variant: in
             raise ValueError(f"{name} must be [B, H, S, D]")
     if k.shape != q.shape or v.shape != q.shape:
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError(f"q, k, v are on different devices: {q.device} {k.device} {v.device}")
     B, H, S, D = q.shape
     if scale is None:
         scale = default_scale(D)
@@ -115,6 +117,9 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None, variant: in
         raise ValueError("out must be a contiguous bf16 tensor shaped like q")
     if lse.dtype != torch.float32 or lse.shape != (B, H, S) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, S] tensor")
+    # the kernel writes through these pointers: they must be device memory of q's GPU
+    if out.device != q.device or lse.device != q.device:
+        raise ValueError(f"out and lse must be on {q.device}, got {out.device} and {lse.device}")
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = attn_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                       B, H, S, D, float(scale), stream, variant)

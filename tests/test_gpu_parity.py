@@ -235,3 +235,10 @@ def test_bad_arguments_raise(daf):
     with pytest.raises(daf.AttnError) as e:
         daf.forward(q, q.clone(), q.clone(), variant=5)
     assert e.value.status == 7
+    # output buffers in host memory are refused before anything is launched
+    with pytest.raises(ValueError):
+        daf.forward(q, q.clone(), q.clone(), out=torch.empty(q.shape, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        daf.forward(q, q.clone(), q.clone(), lse=torch.empty(q.shape[:3], dtype=torch.float32))
+    with pytest.raises(ValueError):
+        daf.forward(q, q.clone().cpu(), q.clone())
