@@ -57,6 +57,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+// Fourth word of a raw buffer resource on gfx9: data format 32 bit (bits
+// 18:15 = 4), no swizzle, no thread-id offset; raw byte-offset loads ignore
+// the format but it must not be the invalid 0.
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr int kD = 128;         // head dimension
 constexpr int kBM = 128;        // query rows per workgroup
@@ -632,10 +636,25 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Raw row max of query block qb over the tile: two v_maximum3 chains over
-// the lane's 4 * BN/16 scores, then the exchange between lane groups.
+// The same for two values at once (the row maxima of two query blocks):
+// the first exchange pairs x0's and x1's lane groups in one swap, which
+// leaves x0's partial maxima in groups 0 and 2 and x1's in groups 1 and 3;
+// after the 32-lane exchange the last 16-lane swap hands out both results
+// without a further maximum. Seven instructions instead of twelve.
+__device__ __forceinline__ void max_over_groups2(float x0, float x1, float& y0, float& y1) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+  const float y = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+  const float z = __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  y0 = __uint_as_float(c[0]);
+  y1 = __uint_as_float(c[1]);
+}
+
+// Raw row max of query block qb over the lane's 4 * BN/16 scores (two
+// v_maximum3 chains), before the exchange between lane groups.
 template <int BN, int QB>
-__device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][QB], int qb) {
+__device__ __forceinline__ float lane_max16(const f32x4 (&s)[BN / 16][QB], int qb) {
   float m0 = __builtin_elementwise_maximum(s[0][qb][0], s[0][qb][1]);
   float m1 = __builtin_elementwise_maximum(s[0][qb][2], s[0][qb][3]);
 #pragma unroll
@@ -643,7 +662,16 @@ __device__ __forceinline__ float tile_max16(const f32x4 (&s)[BN / 16][QB], int q
     m0 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m0, s[kb][qb][0]), s[kb][qb][1]);
     m1 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m1, s[kb][qb][2]), s[kb][qb][3]);
   }
-  return max_over_groups(__builtin_elementwise_maximum(m0, m1));
+  return __builtin_elementwise_maximum(m0, m1);
+}
+
+// Raw row maxima of the wave's query blocks over the tile.
+template <int BN, int QB>
+__device__ __forceinline__ void tile_max16(const f32x4 (&s)[BN / 16][QB], float (&raw)[QB]) {
+  if constexpr (QB == 2)
+    max_over_groups2(lane_max16<BN, QB>(s, 0), lane_max16<BN, QB>(s, 1), raw[0], raw[1]);
+  else
+    raw[0] = max_over_groups(lane_max16<BN, QB>(s, 0));
 }
 
 // P = 2^(s*c - kept) in bf16 as PV B operands, for score blocks kb0 .. kb1-1
@@ -668,11 +696,12 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float 
 // the row max and base update, whose factor for O (already holding
 // PV(i-1)) the next MFMA phase applies, and P(i).
 template <int BN, int QB, int kEmuEvery>
-__device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wave, const char* kg,
-                                             const char* vg, int kfill, int vfill, char* kfree,
+__device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
+                                             __amdgpu_buffer_rsrc_t lrs, int fill, char* kfree,
                                              char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
                                              bf16x8 (&pf)[QB][BN / 32], float (&alpha)[QB],
-                                             bool& rescale, float (&kept)[QB]) {
+                                             bool& rescale, float (&kept)[QB], float (&thr)[QB],
+                                             float thr_gap) {
   constexpr int kTileBytes = BN * kD * 2;
   static_assert(Tiles<BN>::kLoadsPerWave == 8 && BN / 16 == 8, "load spread assumes 128-key tiles");
   // The two groups split the loads so that each phase pair moves one tile:
@@ -685,29 +714,52 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
   // memory path, and a wave's load issue stalls while that path is busy.
   // The wave's 8 loads are therefore spread over the phase, two at a time
   // between parts of the softmax work, instead of being issued up front.
+  //
+  // The loads go through a buffer resource of the group's tensor (K for
+  // group B, V for group A) so that the tile and block offsets stay in
+  // scalar registers; the lane's byte offset `fill` is fixed. They are
+  // issued in every phase: group B's last two (K tiles ntiles and
+  // ntiles + 1) lie past the end of the head's buffer range, so the
+  // hardware's range check turns them into zero fills of a K buffer that
+  // no later QK reads for a used score.
   const bool kside = group == 1;
-  const bool load = kside ? i + 2 < ntiles : i >= 1;
-  const char* src = kside ? kg + int64_t(i + 2) * kTileBytes : vg + int64_t(i) * kTileBytes;
+  const int tile_off = (kside ? i + 2 : i) * kTileBytes;
   char* const dst = kside ? kfree : vcur;
-  const int fill = kside ? kfill : vfill;
   const int stride = kside ? kKBlockPair : kVBlock;
   auto issue2 = [&](int ii) {
-    if (load) {
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int j = 4 * (ii + x) + wave;
-        __builtin_amdgcn_global_load_lds(src + j * 1024 + fill, (lds_void*)(dst + j * stride), 16, 0, 0);
-      }
+    for (int x = 0; x < 2; ++x) {
+      const int j = 4 * (ii + x) + wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(dst + j * stride), 16, fill, tile_off + j * 1024,
+                                               0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
   issue2(0);
+  // Base update with an early out: a row moves its base only when its raw
+  // max reaches `thr` = (kept + threshold) / c, which after the first tiles
+  // is rare, so the factor and the new base are computed only when some
+  // row of the wave needs them (a wave-uniform branch). Otherwise alpha
+  // keeps its stale value, which the MFMA phase does not read.
+  float raw[QB];
+  tile_max16<BN, QB>(s, raw);
+  bool need[QB];
+  uint64_t any = 0;  // one ballot per query block keeps the masks in SGPRs
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) alpha[qb] = base_update_alpha(tile_max16<BN, QB>(s, qb), c, kept[qb]);
-  bool rebased = false;
+  for (int qb = 0; qb < QB; ++qb) {
+    need[qb] = raw[qb] >= thr[qb];
+    any |= __builtin_amdgcn_ballot_w64(need[qb]);
+  }
+  rescale = any != 0;
+  if (rescale) {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) rebased = rebased || alpha[qb] != 1.0f;
-  rescale = __builtin_amdgcn_ballot_w64(rebased) != 0;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m = raw[qb] * c;
+      alpha[qb] = need[qb] ? __builtin_amdgcn_exp2f(kept[qb] - m) : 1.0f;
+      kept[qb] = need[qb] ? m : kept[qb];
+      thr[qb] = need[qb] ? raw[qb] + thr_gap : thr[qb];
+    }
+  }
   issue2(2);
   // The empty assembly statements pin each part of P before the next loads
   // (the compiler would otherwise sink all exponentials below them).
@@ -749,10 +801,11 @@ __device__ __forceinline__ void pp_v_phase(int i, int ntiles, int group, int wav
 // Group A runs M(0) V(0) M(1) V(1) ... M(n); group B starts one barrier
 // later, so interval 2i+1 holds A's V(i) and B's M(i), interval 2i+2 A's
 // M(i+1) and B's V(i). K(i) and V(i) live in buffer i%2. K(i+2) is loaded
-// by group B at the start of its V(i) and awaited at the end of its M(i+1);
-// V(i) is loaded by group A at the start of its V(i) and awaited at its
-// end. Each interval thus moves one tile through the load path (issuing
-// both in one phase stalled that phase for the whole transfer).
+// by group B during its V(i) and awaited at the end of its M(i+1); V(i) is
+// loaded by group A during its V(i) and awaited at its end. Each interval
+// thus moves one tile through the load path (issuing both in one phase
+// stalled that phase for the whole transfer). Before the loop all eight
+// waves load K(0) and K(1).
 //
 // The MFMA phase also takes the row sum of the P it consumes, on the matrix
 // pipe; the softmax phase keeps the row max, the base update and the
@@ -800,13 +853,17 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // V: block 8t + g (+4 for the second read), row col/4 of it, d columns
   // 16db + 4(col%4) .. +3.
   const int v_lane = g * kVBlock + 64 * (col >> 2) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
+  // The tensor this wave's group streams from during its softmax phases, as
+  // a raw buffer over the head (K for group B, V for group A).
+  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(group == 1 ? kg : vg), 0, S * kD * 2, kBufferWord3);
+  const int lfill = group == 1 ? kfill : vfill;
 
   {
 #pragma unroll
     for (int i = 0; i < T::kBlocks / 8; ++i) {
       const int j = 8 * i + wave8;
       __builtin_amdgcn_global_load_lds(kg + j * 1024 + kfill, (lds_void*)(kb0 + j * kKBlockPair), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + j * 1024 + vfill, (lds_void*)(vb0 + j * kVBlock), 16, 0, 0);
       if (ntiles > 1)
         __builtin_amdgcn_global_load_lds(kg + kTileBytes + j * 1024 + kfill,
                                          (lds_void*)(kb1 + j * kKBlockPair), 16, 0, 0);
@@ -828,13 +885,15 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float kept[QB];
+  float kept[QB], thr[QB];
   f32x4 lacc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     kept[qb] = -FLT_MAX;
+    thr[qb] = -__builtin_inff();  // the first tile always sets the base
     lacc[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  const float thr_gap = kRebaseLog2 / c;
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
@@ -856,16 +915,16 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   barrier();
   float alpha[QB];
   bool rescale;
-  pp_v_phase<BN, QB, kEmuEvery>(0, ntiles, group, wave, kg, vg, kfill, vfill, kb0, vb0, c, s, pf, alpha,
-                            rescale, kept);
+  pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lrs, lfill, kb0, vb0, c, s, pf, alpha, rescale,
+                                kept, thr, thr_gap);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
     pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
     if (i == ntiles) break;
-    pp_v_phase<BN, QB, kEmuEvery>(i, ntiles, group, wave, kg, vg, kfill, vfill, k_i, odd ? vb1 : vb0, c, s,
-                              pf, alpha, rescale, kept);
+    pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lrs, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
+                                  rescale, kept, thr, thr_gap);
   }
   if (group == 0) barrier();
 
