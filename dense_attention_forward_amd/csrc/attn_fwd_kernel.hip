@@ -697,7 +697,7 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float 
 // PV(i-1)) the next MFMA phase applies, and P(i).
 template <int BN, int QB, int kEmuEvery>
 __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
-                                             __amdgpu_buffer_rsrc_t lrs, int fill, char* kfree,
+                                             const char* lsrc, int ntiles, int fill, char* kfree,
                                              char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
                                              bf16x8 (&pf)[QB][BN / 32], float (&alpha)[QB],
                                              bool& rescale, float (&kept)[QB], float (&thr)[QB],
@@ -715,23 +715,24 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // The wave's 8 loads are therefore spread over the phase, two at a time
   // between parts of the softmax work, instead of being issued up front.
   //
-  // The loads go through a buffer resource of the group's tensor (K for
-  // group B, V for group A) so that the tile and block offsets stay in
-  // scalar registers; the lane's byte offset `fill` is fixed. They are
-  // issued in every phase: group B's last two (K tiles ntiles and
-  // ntiles + 1) lie past the end of the head's buffer range, so the
-  // hardware's range check turns them into zero fills of a K buffer that
-  // no later QK reads for a used score.
+  // The loads go through a raw buffer resource over the one tile they
+  // fetch (of K for group B, of V for group A, from `lsrc`), so that the
+  // block offsets stay in scalar registers and the lane's byte offset
+  // `fill` is fixed. They are issued in every phase: group B's last two
+  // (K tiles ntiles and ntiles + 1) get a resource of zero length, so the
+  // hardware's range check turns them into zero fills, without a memory
+  // access, of a K buffer that no later QK reads for a used score.
   const bool kside = group == 1;
-  const int tile_off = (kside ? i + 2 : i) * kTileBytes;
+  const int tile = kside ? i + 2 : i;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(lsrc + int64_t(tile) * kTileBytes), 0, tile < ntiles ? kTileBytes : 0, kBufferWord3);
   char* const dst = kside ? kfree : vcur;
   const int stride = kside ? kKBlockPair : kVBlock;
   auto issue2 = [&](int ii) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int j = 4 * (ii + x) + wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (lds_void*)(dst + j * stride), 16, fill, tile_off + j * 1024,
-                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + j * stride), 16, fill, j * 1024, 0, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -853,10 +854,9 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // V: block 8t + g (+4 for the second read), row col/4 of it, d columns
   // 16db + 4(col%4) .. +3.
   const int v_lane = g * kVBlock + 64 * (col >> 2) + 16 * ((col & 3) >> 1) + 8 * (col & 1);
-  // The tensor this wave's group streams from during its softmax phases, as
-  // a raw buffer over the head (K for group B, V for group A).
-  const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<char*>(group == 1 ? kg : vg), 0, S * kD * 2, kBufferWord3);
+  // The tensor this wave's group streams from during its softmax phases
+  // (K for group B, V for group A).
+  const char* const lsrc = group == 1 ? kg : vg;
   const int lfill = group == 1 ? kfill : vfill;
 
   {
@@ -915,7 +915,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   barrier();
   float alpha[QB];
   bool rescale;
-  pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lrs, lfill, kb0, vb0, c, s, pf, alpha, rescale,
+  pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
                                 kept, thr, thr_gap);
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
@@ -923,7 +923,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     char* const v_other = odd ? vb0 : vb1;
     pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
     if (i == ntiles) break;
-    pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lrs, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
+    pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, thr, thr_gap);
   }
   if (group == 0) barrier();
