@@ -120,17 +120,6 @@ __device__ __forceinline__ int v_fill_offset(int l) {
   return q * 256 + (4 * b + x) * 16;
 }
 
-// Base update without touching O: returns the factor O must be multiplied
-// by before the next P.V (1 for rows that keep their base; exactly 1.0, so
-// multiplying by it changes nothing).
-__device__ __forceinline__ float base_update_alpha(float raw_max, float c, float& kept) {
-  const float cand = __builtin_elementwise_maximum(kept, raw_max * c);
-  const bool need = (cand - kept) >= kRebaseLog2;
-  const float alpha = need ? __builtin_amdgcn_exp2f(kept - cand) : 1.0f;
-  kept = need ? cand : kept;
-  return alpha;
-}
-
 template <int BN>
 struct Tiles {
   static constexpr int kBlocks = BN / 4;
