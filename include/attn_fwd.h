@@ -82,8 +82,11 @@ enum attn_variant {
  *   lse     : fp32 [B,H,S] output, natural-log log-sum-exp per query row
  *   B, H, S : batch, heads, sequence length (queries = keys = S)
  *   D       : head dimension, must be 128
- *   scale   : softmax scale applied to q.k, finite and > 0 (usually 1/sqrt(D))
+ *   scale   : softmax scale applied to q.k, finite and > 0 (usually 1/sqrt(D));
+ *             the kernels work in fp32 on scale * log2(e) * q.k, so every such
+ *             product must be finite in fp32 (|scale * q.k| below about 2^127)
  *   stream  : hipStream_t to enqueue on; NULL means the default stream
+ * Inputs must be finite; NaN or Inf in q, k or v gives unspecified output.
  * Returns ATTN_OK or an error code; on error nothing is enqueued (except
  * ATTN_ERR_LAUNCH, where the runtime refused the launch).
  */
