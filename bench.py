@@ -7,15 +7,26 @@ synthetic tensors already resident in HBM when timing starts. Prints one
 JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Two timings:
+  * `value` / `ms_per_step`: the headline workload (16K keys, 16 heads),
+    W untimed launches and at least --min-warm-s seconds of them, then
+    exactly K launches between two HIP events on the launch stream;
+  * `per_workload`: all five workloads the way the B200 attention-kernel
+    article reports its figures ("Performance so far": the median of 6
+    identical runs): after a 0.5 s warm-up, 6 repetitions of at least 20 ms
+    of back-to-back launches each, and their median.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import re
+import statistics
 import sys
 import time
 from pathlib import Path
@@ -28,7 +39,7 @@ import workloads  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak (published)
 METRIC = "attn fwd TFLOP/s (bf16, hd128, non-causal) S=4K/8K/16K; % MFMA peak"
 HEADLINE = "s16k_outliers"
-ALSO = ["s4k", "s8k_peaked", "s16k_outliers"]
+VARIANT_NAMES = {1: "TILE128", 2: "PAIR256", 3: "PAIR256_EXP2EMU", 4: "PAIR128"}
 KERNEL_SOURCES = [ROOT / "dense_attention_forward_amd" / "csrc" / n
                   for n in ("attn_fwd_kernel.hip", "attn_fwd_abi.cpp", "attn_fwd_launch.h")]
 
@@ -58,37 +69,85 @@ def measured_traffic(workload: str):
     return float(m_b.group(1))
 
 
-def time_workload(daf, torch, w, steps: int, warmup: int, min_warm_s: float = 0.0):
-    """Times `steps` launches after `warmup` untimed ones (and, with
-    min_warm_s, more untimed ones until that much wall time has passed: the
-    GPU idles while the inputs are drawn on the host, and its clock takes a
-    while to come back up)."""
+def _launch_all(daf, w, q, k, v, o, lse, n):
+    for _ in range(n):
+        daf.forward(q, k, v, w.scale, out=o, lse=lse)
+
+
+def _device_inputs(torch, w):
     dev = torch.device("cuda", 0)
     q, k, v = (t.to(dev) for t in workloads.make_inputs(w))
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
-    for _ in range(warmup):
-        daf.forward(q, k, v, w.scale, out=o, lse=lse)
+    return q, k, v, o, lse
+
+
+def _warm(daf, torch, w, bufs, min_launches: int, min_s: float) -> float:
+    """At least `min_launches` untimed launches and at least `min_s` seconds
+    of them (the GPU idles while the inputs are drawn on the host, and its
+    clock takes tens of milliseconds of load to come back up). Returns the
+    mean wall time of one launch over the last second of the warm-up."""
+    _launch_all(daf, w, *bufs, max(1, min_launches))
     torch.cuda.synchronize()
     t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < min_warm_s:
-        for _ in range(10):
-            daf.forward(q, k, v, w.scale, out=o, lse=lse)
+    n = 0
+    while True:
+        t0 = time.perf_counter()
+        _launch_all(daf, w, *bufs, 10)
         torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)  # the kernels are enqueued on this stream
+        n += 10
+        if time.perf_counter() - t_warm >= min_s:
+            return (time.perf_counter() - t0) / 10
+
+
+def time_steps(daf, torch, w, steps: int, warmup: int, min_warm_s: float):
+    """The contract's timing: `warmup` untimed launches (and at least
+    min_warm_s seconds of them), then exactly `steps` launches between two
+    HIP events on the stream the kernels are enqueued on (torch's current
+    stream), synchronised on both sides. Returns the mean ms per launch."""
+    bufs = _device_inputs(torch, w)
+    _warm(daf, torch, w, bufs, warmup, min_warm_s)
+    stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
+    torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(steps):
-        daf.forward(q, k, v, w.scale, out=o, lse=lse)
+    _launch_all(daf, w, *bufs, steps)
     end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
+    o, lse = bufs[3], bufs[4]
     ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
-    del q, k, v, o, lse
-    return ms, wall, ok
+    del bufs
+    return ms, ok
+
+
+def median_of_reps(daf, torch, w, reps: int = 6, min_rep_ms: float = 20.0, min_warm_s: float = 0.5):
+    """The article's method ("Performance so far": the median of 6 identical
+    runs): after a time-based warm-up, `reps` repetitions, each a run of
+    back-to-back launches lasting at least min_rep_ms between two HIP events;
+    the median of the per-launch times."""
+    bufs = _device_inputs(torch, w)
+    per_launch_s = _warm(daf, torch, w, bufs, 3, min_warm_s)
+    n = max(3, int(math.ceil(min_rep_ms * 1e-3 / max(per_launch_s, 1e-7))))
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        _launch_all(daf, w, *bufs, n)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) / n)
+    o, lse = bufs[3], bufs[4]
+    ok = bool(torch.isfinite(o).all().item() and torch.isfinite(lse).all().item())
+    del bufs
+    med = statistics.median(times)
+    tf = w.flops / (med * 1e-3) / 1e12
+    return {"tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "ms": round(med, 5),
+            "ms_min": round(min(times), 5), "ms_max": round(max(times), 5), "reps": reps,
+            "launches_per_rep": n, "variant": VARIANT_NAMES.get(daf.pick(w.B, w.H, w.S))}, ok
 
 
 def sustained_mfma(daf, torch, reps: int = 5, iters: int = 2000):
@@ -154,12 +213,15 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--min-warm-s", type=float, default=0.5,
+                    help="untimed launches continue until this many seconds have passed")
     ap.add_argument("--workload", default=HEADLINE, choices=[w.name for w in workloads.WORKLOADS])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip timing the pure MFMA stream (the sustained matrix-core rate)")
-    ap.add_argument("--no-also", action="store_true", help="skip the other sequence lengths")
+    ap.add_argument("--no-also", action="store_true",
+                    help="skip the per-workload medians (all five workloads, 6 repetitions each)")
     ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-baseline sample")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB three times (the "
@@ -191,18 +253,17 @@ def main() -> int:
         return 0
 
     w = workloads.get(args.workload)
-    ms, wall, ok = time_workload(daf, torch, w, args.steps, args.warmup)
-    tflops = w.flops / (ms * 1e-3) / 1e12
     per = {}
+    ok = True
     if not args.no_also:
-        for name in ALSO:
-            if name == w.name:
-                per[name] = {"tflops": round(tflops, 1), "ms": round(ms, 4)}
-                continue
-            wx = workloads.get(name)
-            msx, _, okx = time_workload(daf, torch, wx, max(5, args.steps), 3, min_warm_s=0.3)
+        for wx in workloads.WORKLOADS:
+            per[wx.name], okx = median_of_reps(daf, torch, wx)
             ok = ok and okx
-            per[name] = {"tflops": round(wx.flops / (msx * 1e-3) / 1e12, 1), "ms": round(msx, 4)}
+            print(f"bench: {wx.name} median {per[wx.name]['ms']} ms, {per[wx.name]['tflops']} TFLOP/s",
+                  file=sys.stderr, flush=True)
+    ms, okh = time_steps(daf, torch, w, args.steps, args.warmup, args.min_warm_s)
+    ok = ok and okh
+    tflops = w.flops / (ms * 1e-3) / 1e12
 
     traffic = measured_traffic(w.name)
     line = {

@@ -33,7 +33,7 @@ def hipcc() -> str:
 
 def command(out: Path = LIB, extra: list[str] | None = None) -> list[str]:
     return ([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-             "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)] + DEVICE_FLAGS
+             "-fvisibility=hidden", "-Wall", "-I", str(ROOT / "include"), "-I", str(CSRC)] + DEVICE_FLAGS
             + (extra or []) + [str(s) for s in SOURCES] + ["-o", str(out)])
 
 

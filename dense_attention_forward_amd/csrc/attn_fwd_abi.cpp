@@ -12,8 +12,16 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int kBlockM = 128;
-// Grid limit: the total thread count of a 1-D launch must stay below 2^32.
-constexpr int64_t kMaxWorkgroups = (int64_t(1) << 32) / attn_detail::kThreads - 1;
+// Launch limit: the total thread count of a 1-D grid must stay below 2^32.
+constexpr int64_t kMaxThreads = (int64_t(1) << 32) - 1;
+
+bool basic_shape_ok(int B, int H, int S, int D) {
+  return D == kHeadDim && B >= 1 && H >= 1 && S >= kBlockM && S % kBlockM == 0;
+}
+
+bool grid_ok(int B, int H, int S, int variant) {
+  return attn_detail::launch_threads(B, H, S, variant) <= kMaxThreads;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -22,14 +30,13 @@ bool overlaps(const void* a, uint64_t a_bytes, const void* b, uint64_t b_bytes) 
   return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
 }
 
-}  // namespace
-
-extern "C" int attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
-                              const float* lse, int B, int H, int S, int D, float scale) {
+// Validation for a given resolved variant (AUTO resolves to the pick).
+int check_with_variant(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       int B, int H, int S, int D, float scale, int variant) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULL;
-  if (D != kHeadDim || B < 1 || H < 1 || S < kBlockM || S % kBlockM != 0) return ATTN_ERR_SHAPE;
-  const int64_t workgroups = int64_t(B) * H * (S / kBlockM);
-  if (workgroups > kMaxWorkgroups) return ATTN_ERR_SHAPE;
+  if (!basic_shape_ok(B, H, S, D)) return ATTN_ERR_SHAPE;
+  if (variant == ATTN_VARIANT_AUTO) variant = attn_detail::pick_variant(B, H, S);
+  if (!grid_ok(B, H, S, variant)) return ATTN_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_ALIGN;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return ATTN_ERR_SCALE;
@@ -44,15 +51,22 @@ extern "C" int attn_fwd_check(const void* q, const void* k, const void* v, const
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd_pick(int B, int H, int S) { return attn_detail::pick_variant(B, H, S); }
+}  // namespace
 
-extern "C" int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+extern "C" ATTN_API int attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                                       const float* lse, int B, int H, int S, int D, float scale) {
+  return check_with_variant(q, k, v, o, lse, B, H, S, D, scale, ATTN_VARIANT_AUTO);
+}
+
+extern "C" ATTN_API int attn_fwd_pick(int B, int H, int S) { return attn_detail::pick_variant(B, H, S); }
+
+extern "C" ATTN_API int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                                 int B, int H, int S, int D, float scale, int variant, void* stream) {
   if (variant != ATTN_VARIANT_AUTO && variant != ATTN_VARIANT_TILE128 &&
       variant != ATTN_VARIANT_PAIR256 && variant != ATTN_VARIANT_PAIR256_EXP2EMU &&
       variant != ATTN_VARIANT_PAIR128)
     return ATTN_ERR_VARIANT;
-  const int status = attn_fwd_check(q, k, v, o, lse, B, H, S, D, scale);
+  const int status = check_with_variant(q, k, v, o, lse, B, H, S, D, scale, variant);
   if (status != ATTN_OK) return status;
   attn_detail::Params p;
   p.q = q;
@@ -69,16 +83,17 @@ extern "C" int attn_fwd_variant(const void* q, const void* k, const void* v, voi
   return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+extern "C" ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int H, int S, int D, float scale, void* stream) {
   return attn_fwd_variant(q, k, v, o, lse, B, H, S, D, scale, ATTN_VARIANT_AUTO, stream);
 }
 
-extern "C" const char* attn_status_str(int status) {
+extern "C" ATTN_API const char* attn_status_str(int status) {
   switch (status) {
     case ATTN_OK: return "ok";
     case ATTN_ERR_NULL: return "null pointer argument";
-    case ATTN_ERR_SHAPE: return "unsupported shape (need D == 128, S >= 128, S % 128 == 0, B, H >= 1)";
+    case ATTN_ERR_SHAPE:
+      return "unsupported shape (need D == 128, S >= 128, S % 128 == 0, B, H >= 1, under 2^32 threads)";
     case ATTN_ERR_ALIGN: return "pointer not 16-byte aligned";
     case ATTN_ERR_SCALE: return "scale must be finite and > 0";
     case ATTN_ERR_OVERLAP: return "output buffer overlaps another buffer";

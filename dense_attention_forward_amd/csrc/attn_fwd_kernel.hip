@@ -169,14 +169,18 @@ __device__ __forceinline__ void qk_tile(const char* ksm, int k_lane, const bf16x
 // error on [0, 1] (Remez exchange, with c0 pinned to 1 so integer arguments
 // are exact): 8.6e-5 with these float32 values, far below the 2^-9 of the
 // bf16 rounding that follows. They are produced by exp2_poly_fit.py beside
-// this file. Arguments below -256 give 0, like the flushing exponent unit.
+// this file. The argument is clamped at -127 before it is split, so every
+// argument below -126 (any finite one, however large) gives at most
+// 2^-126, where the exponent unit gives 0; above, the lazy rescale keeps
+// arguments below the rebase threshold (16).
 constexpr float kExp2C0 = 1.0f;
 constexpr float kExp2C1 = 0.6951163411140442f;
 constexpr float kExp2C2 = 0.22764700651168823f;
 constexpr float kExp2C3 = 0.07706519961357117f;
 __device__ __forceinline__ float exp2_poly(float x) {
-  const float n = fmaxf(__builtin_floorf(x), -256.0f);
-  const float f = x - n;
+  const float xc = __builtin_fmaxf(x, -127.0f);
+  const float n = __builtin_floorf(xc);
+  const float f = xc - n;
   float p = __builtin_fmaf(kExp2C3, f, kExp2C2);
   p = __builtin_fmaf(p, f, kExp2C1);
   p = __builtin_fmaf(p, f, kExp2C0);
@@ -948,16 +952,41 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #endif
 
 
+namespace {
+// PAIR256: two 128-row query tiles per workgroup (two 16-query blocks per
+// wave); PAIR128: two 64-row tiles (one block per wave), for grids too
+// small to fill the GPU with 256-row workgroups. TILE128: one 128-row tile.
+bool is_pair(int variant) {
+  return variant == ATTN_VARIANT_PAIR256 || variant == ATTN_VARIANT_PAIR256_EXP2EMU ||
+         variant == ATTN_VARIANT_PAIR128;
+}
+int pair_rows(int variant) { return variant == ATTN_VARIANT_PAIR128 ? 64 : 128; }
+int64_t workgroups(int B, int H, int S, int variant) {
+  if (!is_pair(variant)) return int64_t(B) * H * (S / kBM);
+  const int tiles = S / pair_rows(variant);
+  return int64_t(B) * H * ((tiles + 1) / 2);
+}
+}  // namespace
+
+int64_t launch_threads(int B, int H, int S, int variant) {
+  return workgroups(B, H, S, variant) * (is_pair(variant) ? 2 * kThreads : kThreads);
+}
+
 // PAIR256 once its workgroups (pairs of 128-row tiles) fill the GPU's CUs
 // once; below that PAIR128 (pairs of 64-row tiles), down to launches of a
 // handful of workgroups, which one 128-row tile per workgroup serves a little
 // faster. Measured: from 256 PAIR256 workgroups up PAIR256 is fastest; below,
 // PAIR128 beats TILE128 by 13-48% at 32-256 workgroups; at 2 workgroups
-// (S = 256, one head) TILE128 is 5% ahead.
+// (S = 256, one head) TILE128 is 5% ahead. A grid so large that PAIR256's
+// launch would reach 2^32 threads (only possible when S / 128 is odd, which
+// leaves half of the last workgroup of each head idle) takes TILE128, which
+// needs fewer threads.
 int pick_variant(int B, int H, int S) {
   const int64_t pair_wgs = int64_t(B) * H * ((S / kBM + 1) / 2);
   const int64_t half_pair_wgs = int64_t(B) * H * (S / (2 * 64));
-  if (pair_wgs >= ATTN_PP_MIN_WGS) return ATTN_VARIANT_PAIR256;
+  if (pair_wgs >= ATTN_PP_MIN_WGS)
+    return launch_threads(B, H, S, ATTN_VARIANT_PAIR256) < (int64_t(1) << 32) ? ATTN_VARIANT_PAIR256
+                                                                             : ATTN_VARIANT_TILE128;
   if (half_pair_wgs >= 16) return ATTN_VARIANT_PAIR128;
   return ATTN_VARIANT_TILE128;
 }
@@ -986,15 +1015,10 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   const auto* k = static_cast<const char*>(p.k);
   const auto* v = static_cast<const char*>(p.v);
   auto* o = static_cast<__bf16*>(p.o);
-  if (p.variant == ATTN_VARIANT_PAIR256 || p.variant == ATTN_VARIANT_PAIR256_EXP2EMU ||
-      p.variant == ATTN_VARIANT_PAIR128) {
-    // PAIR256: two 128-row query tiles per workgroup (two 16-query blocks
-    // per wave); PAIR128: two 64-row tiles (one block per wave), for grids
-    // too small to fill the GPU with 256-row workgroups.
-    const int rows = p.variant == ATTN_VARIANT_PAIR128 ? 64 : 128;
-    const int tiles = p.S / rows;
+  const int nwg = int(workgroups(p.B, p.H, p.S, p.variant));  // below 2^32 / 256 (checked)
+  if (is_pair(p.variant)) {
+    const int tiles = p.S / pair_rows(p.variant);
     const int npairs = (tiles + 1) / 2;
-    const int nwg = int(int64_t(p.B) * p.H * npairs);
     // PAIR256_EXP2EMU: one exponential in four on the FMA pipe
     auto kernel = p.variant == ATTN_VARIANT_PAIR256   ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, 0>
                   : p.variant == ATTN_VARIANT_PAIR128 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 1, 0>
@@ -1002,7 +1026,6 @@ hipError_t launch(const Params& p, hipStream_t stream) {
     return launch_kernel(kernel, dim3(nwg), dim3(2 * kThreads), stream, q, k, v, o, p.lse, p.S, tiles,
                          npairs, nwg, c);
   }
-  const int nwg = p.B * p.H * qtiles;
   return launch_kernel(attn_fwd_kernel<BN>, dim3(nwg), dim3(kThreads), stream, q, k, v, o, p.lse, p.S,
                        qtiles, nwg, c);
 }

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(const bf16x8* __restrict
 
 }  // namespace
 
-extern "C" int attn_mfma_rate(const void* operands, float* sink, int workgroups, int iters,
+extern "C" ATTN_API int attn_mfma_rate(const void* operands, float* sink, int workgroups, int iters,
                               void* stream) {
   if (!operands || !sink) return ATTN_ERR_NULL;
   if ((reinterpret_cast<uintptr_t>(operands) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3))

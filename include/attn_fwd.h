@@ -32,6 +32,14 @@
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
 
+/* The library is built with hidden symbol visibility; exactly the functions
+ * declared with ATTN_API in this directory's headers are exported. */
+#if defined(__GNUC__) || defined(__clang__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -40,7 +48,8 @@ enum attn_status {
   ATTN_OK = 0,
   ATTN_ERR_NULL = 1,       /* a pointer argument is NULL */
   ATTN_ERR_SHAPE = 2,      /* D != 128, S < 128, S % 128 != 0, B < 1, H < 1, or the
-                              grid (B*H*S/128 workgroups) exceeds the launch limit */
+                              launch of the kernel variant used would have 2^32 or
+                              more threads (about B*H*S >= 2^32 for every variant) */
   ATTN_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned */
   ATTN_ERR_SCALE = 4,      /* scale is not finite or not > 0 (the row max is taken
                               over raw scores and scaled afterwards, which needs a
@@ -79,7 +88,8 @@ enum attn_variant {
  * Dense attention forward.
  *   q, k, v : bf16 [B,H,S,D] inputs (device, 16-byte aligned, read only)
  *   o       : bf16 [B,H,S,D] output (device, 16-byte aligned)
- *   lse     : fp32 [B,H,S] output, natural-log log-sum-exp per query row
+ *   lse     : fp32 [B,H,S] output, natural-log log-sum-exp per query row,
+ *             ln sum_j exp(scale * q_i . k_j) (see "Accuracy" below)
  *   B, H, S : batch, heads, sequence length (queries = keys = S)
  *   D       : head dimension, must be 128
  *   scale   : softmax scale applied to q.k, finite and > 0 (usually 1/sqrt(D));
@@ -89,8 +99,22 @@ enum attn_variant {
  * Inputs must be finite; NaN or Inf in q, k or v gives unspecified output.
  * Returns ATTN_OK or an error code; on error nothing is enqueued (except
  * ATTN_ERR_LAUNCH, where the runtime refused the launch).
+ *
+ * Accuracy. The unnormalised probabilities p_j are rounded to bf16 before
+ * they multiply v (as in the article, Chapter 1 section B), and the row sum
+ * adds these same rounded values (the article adds the unrounded ones), so
+ * o is a convex combination of the rows of v with weights off by at most
+ * 2^-8 relative each. lse is taken from
+ * that same sum: its absolute error is at most -ln(1 - 2^-8) ~= 3.9e-3 (the
+ * worst case, reached when one or a few keys carry nearly all of a row's
+ * weight and their p round the same way), plus fp32 rounding of order
+ * 1e-6 * |lse|. Where many keys share the weight their rounding errors
+ * cancel: on normally distributed inputs the error is of order 1e-5 to 1e-4
+ * relative. A caller that merges partial results by their lse (a split
+ * over keys) sees the merge weights off by at most about 0.4%, the same
+ * order as the bf16 rounding of o itself.
  */
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S, int D, float scale, void* stream);
 
 /*
@@ -98,27 +122,28 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * arguments, layout, ownership and errors as attn_fwd, plus
  * ATTN_ERR_VARIANT for an unknown variant. For tests and tuning.
  */
-int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+ATTN_API int attn_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                      int B, int H, int S, int D, float scale, int variant, void* stream);
 
 /*
  * The variant attn_fwd picks for a shape (pure host code): PAIR256 when its
- * grid of 128-row tile pairs has at least 256 workgroups, else PAIR128 when
- * its grid of 64-row tile pairs has at least 16, else TILE128.
+ * grid of 128-row tile pairs has at least 256 workgroups (unless that grid
+ * would reach 2^32 threads, then TILE128), else PAIR128 when its grid of
+ * 64-row tile pairs has at least 16, else TILE128.
  * Returns ATTN_VARIANT_TILE128, ATTN_VARIANT_PAIR128 or ATTN_VARIANT_PAIR256.
  */
-int attn_fwd_pick(int B, int H, int S);
+ATTN_API int attn_fwd_pick(int B, int H, int S);
 
 /*
  * The argument validation of attn_fwd on its own: pure host code that
  * touches no device memory and needs no GPU. Returns the status attn_fwd
  * would return before launching.
  */
-int attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
+ATTN_API int attn_fwd_check(const void* q, const void* k, const void* v, const void* o,
                    const float* lse, int B, int H, int S, int D, float scale);
 
 /* A static, human-readable name for a status code (never NULL). */
-const char* attn_status_str(int status);
+ATTN_API const char* attn_status_str(int status);
 
 #ifdef __cplusplus
 }

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-int attn_mfma_rate(const void* operands, float* sink, int workgroups, int iters, void* stream);
+ATTN_API int attn_mfma_rate(const void* operands, float* sink, int workgroups, int iters, void* stream);
 
 #ifdef __cplusplus
 }

@@ -85,6 +85,7 @@ def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
     rowsum = torch.zeros(M, dtype=torch.float64)
     acc = torch.zeros((M, v.shape[1]), dtype=torch.float64)
     rebases = 0
+    row_rebases = torch.zeros(M, dtype=torch.int64)    # rebases after the first tile, per row
     for j0 in range(0, S, block_n):
         kt = k[j0:j0 + block_n]
         vt = v[j0:j0 + block_n]
@@ -100,6 +101,7 @@ def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
             acc = acc * alpha[:, None]
             kept = torch.where(need, cand, kept)
             rebases += int(need.sum())
+            row_rebases += need.to(torch.int64)
         p = _ftz(torch.exp2(s_raw * c - kept[:, None]))  # unnormalised P against the kept base
         if stats is not None:
             stats["max_p"] = max(stats.get("max_p", 0.0), float(p.max()))
@@ -108,6 +110,7 @@ def online_tile(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sigma: float,
         acc = acc + pv @ vt
     if stats is not None:
         stats["rebases"] = stats.get("rebases", 0) + rebases
+        stats.setdefault("row_rebases", []).append(row_rebases)
     o = acc / rowsum[:, None]
     lse = (kept + torch.log2(rowsum)) * math.log(2.0)   # natural log of the denominator
     return o, lse

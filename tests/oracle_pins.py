@@ -16,11 +16,19 @@ What fixes each expected value:
     definition (a shift added to every score, reordering, linearity of the
     weighted mean, a saturated softmax);
   * brute_force: scalar Python loops over a tiny case;
-  * sdpa: torch's scaled_dot_product_attention and logsumexp in float64.
+  * sdpa: torch's scaled_dot_product_attention and logsumexp in float64;
+  * inexact_scale: the two-key closed form with a scale (0.1) that float32
+    cannot hold exactly, at scores large enough that using the unrounded
+    scale moves O and lse far beyond the tolerance.
+
+Pins of the probability matrix take ``probs(q, k, scale) -> P`` instead
+(PROB_PINS): the two-key sigmoid closed form, the orthogonal-key closed
+form, and P.V against the brute-force weighted mean.
 """
 from __future__ import annotations
 
 import math
+import struct
 
 import torch
 
@@ -214,6 +222,88 @@ def pin_sdpa(attn):
     _close(lse, want_lse, 1e-12, "sdpa lse")
 
 
+def _f32(x: float) -> float:
+    """x rounded to the nearest float32 (the scale the kernel receives)."""
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def pin_inexact_scale(attn):
+    """Scale 0.1 is not a float32 value; the contract is that the scores use
+    its float32 rounding sigma = 0.100000001490116... Two keys 0 and a with
+    q = 1 (D = 1): the weight of key 1 is sigmoid(sigma a) and lse =
+    softplus(sigma a). At a = 10 the unrounded scale moves O by ~5e-9, at
+    a = 1e6 it moves lse by ~1.5e-3; both far above the tolerances."""
+    scale = 0.1
+    sigma = _f32(scale)
+    assert sigma != scale
+    v0, v1 = 0.25, -1.5
+    for a, o_tol, lse_tol in ((10.0, 1e-13, 1e-13), (1e6, 1e-13, 1e-9)):
+        q = _t([[[[1.0]]]])
+        k = _t([[[[0.0], [a]]]])
+        v = _t([[[[v0], [v1]]]])
+        o, lse = attn(q, k, v, scale)
+        x = sigma * a
+        w1 = 1.0 / (1.0 + math.exp(-x))
+        _close(o, _t([[[[v0 + (v1 - v0) * w1]]]]), o_tol, f"inexact_scale O a={a}")
+        _close(lse, _t([[[x + math.log1p(math.exp(-x))]]]), lse_tol, f"inexact_scale lse a={a}")
+
+
 ALL_PINS = [pin_two_keys, pin_orthogonal_keys, pin_q_zero, pin_identical_keys, pin_key_shift,
             pin_permutation, pin_affine_v, pin_single_key, pin_dominant_key, pin_brute_force,
-            pin_sdpa]
+            pin_sdpa, pin_inexact_scale]
+
+
+# ---- pins of the probability matrix: probs(q, k, scale) -> P [B, H, S_q, S_k] ----
+
+def pin_probs_two_keys(probs):
+    """q = 1 (D = 1), keys 0 and a: P = (1 - w, w) with w = sigmoid(sigma a),
+    for an exact scale (0.5) and an inexact one (0.1, sigma its float32
+    rounding), including sigma a = 1000 where exp without the max overflows."""
+    for scale in (0.5, 0.1):
+        sigma = _f32(scale)
+        for a in (0.0, 1.0, -3.0, 10.0, 2000.0 if scale == 0.5 else 10000.0):
+            p = probs(_t([[[[1.0]]]]), _t([[[[0.0], [a]]]]), scale)
+            x = sigma * a
+            w1 = 1.0 / (1.0 + math.exp(-x)) if x >= 0 else math.exp(x) / (1.0 + math.exp(x))
+            _close(p, _t([[[[1.0 - w1, w1]]]]), 1e-15, f"probs two_keys scale={scale} a={a}")
+
+
+def pin_probs_orthogonal_keys(probs):
+    """K = c I (4 keys, D = 4), query i = unit vector pi(i): row i has
+    e^(sigma c) / (e^(sigma c) + 3) at column pi(i) and 1 / (e^(sigma c) + 3)
+    elsewhere. A transposed P (softmax over queries) differs, since pi is a
+    cycle and the rows are not symmetric."""
+    c = 3.0
+    pi = [1, 2, 3, 0]
+    q = torch.zeros((1, 1, 4, 4), dtype=F64)
+    for i, j in enumerate(pi):
+        q[0, 0, i, j] = 1.0
+    k = (c * torch.eye(4, dtype=F64)).reshape(1, 1, 4, 4)
+    # a fifth key that no query sees (zero score) makes P non-square
+    k = torch.cat([k, torch.zeros((1, 1, 1, 4), dtype=F64)], dim=2)
+    p = probs(q, k, SCALE)
+    big = math.exp(SCALE * c)
+    want = torch.full((4, 5), 1.0 / (big + 4.0), dtype=F64)
+    for i in range(4):
+        want[i, pi[i]] = big / (big + 4.0)
+    _close(p[0, 0], want, 1e-15, "probs orthogonal_keys")
+
+
+def pin_probs_weighted_mean(probs):
+    """P.V equals the brute-force softmax-weighted mean (scalar math.exp loops)."""
+    gen = torch.Generator().manual_seed(20)
+    q = torch.randn((1, 1, 3, 4), generator=gen, dtype=F64) * 2
+    k = torch.randn((1, 1, 6, 4), generator=gen, dtype=F64) * 2
+    v = torch.randn((1, 1, 6, 2), generator=gen, dtype=F64)
+    p = probs(q, k, 0.3)
+    sigma = _f32(0.3)
+    Q, K, V = q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist()
+    pv = p[0, 0] @ v[0, 0]
+    for i in range(3):
+        w = [math.exp(sigma * sum(Q[i][d] * K[j][d] for d in range(4))) for j in range(6)]
+        z = sum(w)
+        for e in range(2):
+            _close(pv[i, e], sum(w[j] * V[j][e] for j in range(6)) / z, 1e-13, f"probs weighted_mean [{i},{e}]")
+
+
+PROB_PINS = [pin_probs_two_keys, pin_probs_orthogonal_keys, pin_probs_weighted_mean]

@@ -43,13 +43,25 @@ def test_header_declares_the_boundary():
                                           "attn_fwd_variant", "attn_fwd_pick"}
 
 
-def test_every_declared_symbol_is_exported(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", str(lib.LIB_PATH)], capture_output=True,
+def _exported_functions(path):
+    """Names of the functions the shared library exports (defined, dynamic, text)."""
+    out = subprocess.run(["nm", "-D", "--defined-only", str(path)], capture_output=True,
                          text=True, check=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    return {line.split()[-1] for line in out.splitlines()
+            if line.strip() and line.split()[-2] in ("T", "W")}
+
+
+def test_every_declared_symbol_is_exported(lib):
+    exported = _exported_functions(lib.LIB_PATH)
     for name in _declared_functions():
         assert name in exported, name
         assert getattr(lib.lib(), name) is not None
+
+
+def test_only_declared_symbols_are_exported(lib):
+    """The library is built with hidden visibility: nothing but the C ABI of
+    the headers (no C++ internals) is visible to a client."""
+    assert _exported_functions(lib.LIB_PATH) == set(_declared_functions())
 
 
 # Fake, aligned, non-overlapping "device" addresses: only compared, never dereferenced.
@@ -65,6 +77,30 @@ def _check(lib, q=Q, k=K, v=V, o=O, l=L, b=B, h=H, s=S, d=D, scale=SC):
 
 def test_check_ok(lib):
     assert _check(lib) == 0
+
+
+# Far-apart fake addresses for huge shapes (2^30 rows of 256 bytes each = 256 GiB per tensor).
+FAR = [(i + 1) << 40 for i in range(5)]
+
+
+def test_grid_limit_per_variant(lib):
+    """B*H*S = 2^30 rows: one 128-row tile per 4-wave workgroup needs 2^31
+    threads, while the pairs of 64-row tiles of PAIR128 (8 waves per 128
+    rows) would need 2^32, beyond the launch limit: a forced PAIR128 call
+    is refused as a shape error before any launch, and the library's own
+    pick (which falls back from PAIR256, also 2^32 threads at S = 128)
+    accepts the shape."""
+    q, k, v, o, l = FAR
+    b, h, s = 1, 1 << 23, 128
+    assert lib.check(q, k, v, o, l, b, h, s, D, SC) == 0
+    assert lib.pick(b, h, s) == lib.VARIANT_TILE128
+    for variant in (lib.VARIANT_PAIR128, lib.VARIANT_PAIR256, lib.VARIANT_PAIR256_EXP2EMU):
+        assert lib.attn_fwd_raw(q, k, v, o, l, b, h, s, D, SC, 0, variant=variant) == 2
+    # twice the rows: every variant would need 2^32 threads or more
+    assert lib.check(q, k, v, o, l, 2, h, s, D, SC) == 2
+    # at S = 256 PAIR256 needs no more threads than TILE128 and is kept
+    assert lib.pick(1, 1 << 22, 256) == lib.VARIANT_PAIR256
+    assert lib.check(q, k, v, o, l, 1, 1 << 22, 256, D, SC) == 0
 
 
 @pytest.mark.parametrize("arg", ["q", "k", "v", "o", "l"])

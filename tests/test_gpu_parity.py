@@ -189,24 +189,59 @@ def test_dominant_key(daf):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("direction", ["rising", "falling", "late_spike"])
+@pytest.mark.parametrize("direction", ["rising", "staircase", "falling", "late_spike"])
 def test_rebase_patterns(daf, direction, variant):
-    """Rising key norms force a rebase on most tiles; falling ones make later
-    P flush to zero; a spike in the last tile forces one late, large rebase."""
+    """Key-norm patterns for the lazy rescale at the kernels' threshold of
+    16 base-2 units. "rising" (a linear ramp) moves each row's base about
+    once after its first tile; "staircase" multiplies each 128-key tile's
+    norms by a growing step, so nearly every row moves its base on most
+    tiles (at least 4 times for 95% of rows, counted with the tile-by-tile
+    model at threshold 16 before the GPU runs); "falling" makes later P
+    flush to zero; a spike in the last tile forces one late, large rebase."""
+    from oracle import online_model
+    from workloads import staircase_keys
     _say(f"case rebase {direction} variant={variant}")
     S = 1024
     q, k, v = make_random(1, 2, S, 128, seed=26)
     kf = k.float()
     if direction == "rising":
-        kf = kf * torch.linspace(0.1, 8.0, S).reshape(1, 1, S, 1)
+        k = (kf * torch.linspace(0.1, 8.0, S).reshape(1, 1, S, 1)).to(torch.bfloat16)
+    elif direction == "staircase":
+        k = staircase_keys(k)
+        for block_n in (64, 128):  # the key-tile lengths of the two kernels
+            stats = {}
+            online_model.online_attention(q, k, v, DEFAULT_SCALE, block_n=block_n, thresh_log2=16.0,
+                                          stats=stats)
+            per_row = torch.cat(stats["row_rebases"]).float()
+            assert (per_row >= 4).float().mean().item() >= 0.95
     elif direction == "falling":
-        kf = kf * torch.linspace(8.0, 0.1, S).reshape(1, 1, S, 1)
+        k = (kf * torch.linspace(8.0, 0.1, S).reshape(1, 1, S, 1)).to(torch.bfloat16)
     else:
         kf[:, :, S - 5] = q.float()[:, :, 0] * 4.0
-    k = kf.to(torch.bfloat16)
+        k = kf.to(torch.bfloat16)
     o, lse = _run(daf, q, k, v, variant=variant)
     o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
     _assert_parity(o, lse, o_ref, lse_ref, f"rebase {direction} v{variant}")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_lse_bound_with_one_dominant_key(daf, variant):
+    """The worst case of the LSE taken from the sum of the bf16-rounded P:
+    one dominant key whose p is not exact in bf16, at lse ~= 0.92. The LSE
+    error must stay within the bound the header states, -ln(1 - 2^-8) plus
+    fp32 rounding; O must meet its bar. (The tile-by-tile model of the same
+    arithmetic is off by about 3.4e-3 here.)"""
+    from workloads import dominant_key_small_lse_case
+    _say(f"case LSE bound, one dominant key, variant={variant}")
+    q1, k, v = dominant_key_small_lse_case()
+    q = q1.expand(1, 1, k.shape[2], 128).contiguous()  # every query row is e_0
+    o, lse = _run(daf, q, k, v, variant=variant)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    err = (lse.double() - lse_ref).abs().max().item()
+    oerr = (o.double() - o_ref).abs()
+    _say(f"  LSE max-abs {err:.3e} (lse {lse_ref[0, 0, 0].item():.4f}); O max-abs {oerr.max().item():.3e}")
+    assert err <= -math.log1p(-2.0 ** -8) + 1e-5
+    assert oerr.max().item() <= O_MAX and oerr.mean().item() <= O_MEAN
 
 
 @pytest.mark.parametrize("scale", [1.0, 0.25, 1e-3])

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 from oracle import online_model
-from workloads import DEFAULT_SCALE, make_random
+from workloads import DEFAULT_SCALE, dominant_key_small_lse_case, make_random
 
 GOLDEN = json.loads((Path(__file__).parent / "golden" / "page_values.json").read_text())
 
@@ -110,7 +110,7 @@ def test_lazy_rescale_equals_two_pass(case, block_n):
     assert stats["max_p"] <= 2.0 ** 8 * (1 + 1e-12)
 
 
-@pytest.mark.parametrize("thresh", [0.0, 8.0, 15.0])
+@pytest.mark.parametrize("thresh", [0.0, 8.0, 15.0, 16.0])
 def test_threshold_does_not_change_result(thresh):
     q, k, v = _ramp_inputs(384)
     o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, thresh_log2=thresh)
@@ -166,3 +166,45 @@ def test_rounded_rowsum_error_on_outlier_recipe():
     assert (lse - lse_ref).abs().max().item() <= -math.log1p(-2.0 ** -8)
     rel = ((lse - lse_ref).abs() / lse_ref.abs().clamp_min(1.0)).max().item()
     assert rel < 1e-3 / 2
+
+
+def test_staircase_rebases_repeatedly_at_threshold_16():
+    """The staircase key recipe of the GPU rebase tests (key norms rising
+    tile by tile) makes nearly every row rebase on most tiles at the
+    kernels' threshold of 16, for both key-tile lengths the kernels use, and
+    the result still equals the two-pass oracle."""
+    from workloads import staircase_keys
+    q, k, v = make_random(1, 2, 1024, 128, seed=26)
+    k = staircase_keys(k)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    for block_n in (64, 128):
+        stats = {}
+        o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, block_n=block_n,
+                                               thresh_log2=16.0, stats=stats)
+        per_row = torch.cat(stats["row_rebases"])
+        assert per_row.numel() == 2 * 1024
+        assert (per_row >= 4).float().mean().item() >= 0.95, per_row.float().mean()
+        assert per_row.float().median().item() >= 5
+        assert (o - o_ref).abs().max().item() < 1e-12
+        assert ((lse - lse_ref).abs() / lse_ref.abs()).max().item() < 1e-13
+
+
+def test_rounded_rowsum_lse_bound_is_reached():
+    """Worst case of the rounded-P row sum: with one dominant key whose
+    unnormalised p is rounded to bf16, the LSE taken from that sum is off by
+    close to the bound -ln(1 - 2^-8) ~= 3.9e-3 (here about 3.4e-3, above the
+    1e-3 relative bar at |lse| < 1), while O stays far inside its bar."""
+    q, k, v = dominant_key_small_lse_case()
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    assert 0.9 < lse_ref.item() < 0.95
+    bound = -math.log1p(-2.0 ** -8)
+    for block_n in (64, 128):
+        o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, block_m=1, block_n=block_n,
+                                               thresh_log2=16.0, p_to_bf16=True, rowsum_of_rounded=True)
+        err = abs(lse.item() - lse_ref.item())
+        assert 2.5e-3 < err <= bound
+        assert (o - o_ref).abs().max().item() < 1e-3
+        # the article's unrounded sum gets the LSE right in this case
+        _, lse_u = online_model.online_attention(q, k, v, DEFAULT_SCALE, block_m=1, block_n=block_n,
+                                                 thresh_log2=16.0, p_to_bf16=True)
+        assert abs(lse_u.item() - lse_ref.item()) < 1e-12

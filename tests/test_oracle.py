@@ -27,6 +27,23 @@ def test_small_blocks_match_one_block():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("pin", oracle_pins.PROB_PINS, ids=lambda p: p.__name__)
+def test_probs_pin(pin):
+    pin(oracle.attention_probs)
+
+
+def test_probs_times_v_is_attention():
+    """The probability matrix and the two-pass attention agree: P.V = O, and
+    the log of each row's largest-P denominator matches lse (P_max = e^(s_max - lse))."""
+    q, k, v = make_random(1, 2, 128, 128, seed=2005, qk_std=2.0)
+    p = oracle.attention_probs(q, k, DEFAULT_SCALE)
+    o, lse = oracle.attention(q, k, v, DEFAULT_SCALE)
+    assert (p @ v.double() - o).abs().max().item() < 1e-13
+    s = (q.double() @ k.double().transpose(-1, -2)) * oracle.sigma_of(DEFAULT_SCALE)
+    m = s.max(dim=-1).values
+    assert (torch.log(p.max(dim=-1).values) - (m - lse)).abs().max().item() < 1e-12
+
+
 def test_rows_of_p_sum_to_one():
     q, k, _ = make_random(1, 2, 128, 128, seed=2002, qk_std=2.0)
     p = oracle.attention_probs(q, k, DEFAULT_SCALE)

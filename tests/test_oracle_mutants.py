@@ -8,9 +8,10 @@ import torch
 from tests import oracle_pins
 
 
-def _make(head_fn):
+def _make(head_fn, raw_scale=False):
     def attn(q, k, v, scale):
-        sigma = float(torch.tensor(scale, dtype=torch.float32).item())
+        # raw_scale plants the mistake of using the scale without its float32 rounding
+        sigma = scale if raw_scale else float(torch.tensor(scale, dtype=torch.float32).item())
         B, H, Sq, _ = q.shape
         o = torch.empty((B, H, Sq, v.shape[3]), dtype=torch.float64)
         lse = torch.empty((B, H, Sq), dtype=torch.float64)
@@ -119,8 +120,8 @@ MUTANTS = [_no_scale, _scale_squared, _lse_log2, _lse_without_max, _no_max_trick
            _mean_instead_of_sum]
 
 
-def _caught(attn):
-    for pin in oracle_pins.ALL_PINS:
+def _caught(attn, pins=oracle_pins.ALL_PINS):
+    for pin in pins:
         try:
             pin(attn)
         except (AssertionError, RuntimeError, IndexError, ValueError):
@@ -135,3 +136,65 @@ def test_reference_copy_passes_all_pins():
 @pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m.__name__)
 def test_mutant_is_caught(mutant):
     assert _caught(_make(mutant)) is not None, f"no pin catches {mutant.__name__}"
+
+
+def test_unrounded_scale_is_caught():
+    """A copy that uses the scale as given instead of its float32 value."""
+    assert _caught(_make(_ok, raw_scale=True)) == "pin_inexact_scale"
+
+
+# ---- mutants of the probability matrix ----
+
+def _sigma(scale):
+    return float(torch.tensor(scale, dtype=torch.float32).item())
+
+
+def _probs_ok(q, k, scale):
+    s = (q.double() @ k.double().transpose(-1, -2)) * _sigma(scale)
+    e = torch.exp(s - s.max(dim=-1, keepdim=True).values)
+    return e / e.sum(dim=-1, keepdim=True)
+
+
+def _probs_no_scale(q, k, scale):
+    return _probs_ok(q, k, 1.0)
+
+
+def _probs_raw_scale(q, k, scale):
+    s = (q.double() @ k.double().transpose(-1, -2)) * scale
+    e = torch.exp(s - s.max(dim=-1, keepdim=True).values)
+    return e / e.sum(dim=-1, keepdim=True)
+
+
+def _probs_exp2(q, k, scale):
+    s = (q.double() @ k.double().transpose(-1, -2)) * _sigma(scale)
+    e = torch.exp2(s - s.max(dim=-1, keepdim=True).values)
+    return e / e.sum(dim=-1, keepdim=True)
+
+
+def _probs_over_queries(q, k, scale):
+    s = (q.double() @ k.double().transpose(-1, -2)) * _sigma(scale)
+    e = torch.exp(s - s.max(dim=-2, keepdim=True).values)
+    return e / e.sum(dim=-2, keepdim=True)
+
+
+def _probs_no_max_trick(q, k, scale):
+    e = torch.exp((q.double() @ k.double().transpose(-1, -2)) * _sigma(scale))
+    return e / e.sum(dim=-1, keepdim=True)
+
+
+def _probs_unnormalised(q, k, scale):
+    s = (q.double() @ k.double().transpose(-1, -2)) * _sigma(scale)
+    return torch.exp(s - s.max(dim=-1, keepdim=True).values)
+
+
+PROB_MUTANTS = [_probs_no_scale, _probs_raw_scale, _probs_exp2, _probs_over_queries,
+                _probs_no_max_trick, _probs_unnormalised]
+
+
+def test_reference_probs_copy_passes():
+    assert _caught(_probs_ok, oracle_pins.PROB_PINS) is None
+
+
+@pytest.mark.parametrize("mutant", PROB_MUTANTS, ids=lambda m: m.__name__)
+def test_probs_mutant_is_caught(mutant):
+    assert _caught(mutant, oracle_pins.PROB_PINS) is not None, f"no pin catches {mutant.__name__}"

@@ -134,3 +134,33 @@ def make_random(B: int, H: int, S: int, D: int, seed: int, qk_std: float = 1.0,
     w = Workload("adhoc", seed - 1000, B, H, S, D, "normal", qk_std, v_dist,
                  outlier_frac, outlier_mult, DEFAULT_SCALE)
     return make_inputs(w)
+
+
+def staircase_keys(k: torch.Tensor, tile: int = 128, step: float = 7.0) -> torch.Tensor:
+    """K with its rows in key tile t (of `tile` keys) multiplied by
+    0.25 + step * t, cast back to bf16: each tile's largest scores rise well
+    above the previous tile's, so an online softmax moves its base on nearly
+    every tile (a test pattern for the lazy rescale)."""
+    S = k.shape[2]
+    f = 0.25 + step * (torch.arange(S) // tile).to(torch.float32)
+    return (k.float() * f.reshape(1, 1, S, 1)).to(torch.bfloat16).contiguous()
+
+
+def dominant_key_small_lse_case():
+    """One query e_0 over 256 keys whose first components are -45.25 (key 0),
+    10.375 (key 200) and -340 (all others): key 200 carries nearly all the
+    weight, lands 7.1 base-2 units above the first tile's max (below the
+    rebase threshold, so its p = 2^7.1 is not exact in bf16), and lse is
+    close to 0.92, where the relative LSE bar is an absolute one. Every value
+    is exact in bf16."""
+    S = 256
+    q = torch.zeros((1, 1, 1, 128))
+    q[0, 0, 0, 0] = 1.0
+    k = torch.zeros((1, 1, S, 128))
+    k[0, 0, :, 0] = -340.0
+    k[0, 0, 0, 0] = -45.25
+    k[0, 0, 200, 0] = 10.375
+    v = torch.zeros((1, 1, S, 128))
+    v[0, 0, :, 1] = torch.linspace(-1.0, 1.0, S)
+    v[0, 0, 200, 2] = 1.0
+    return tuple(t.to(torch.bfloat16) for t in (q, k, v))
