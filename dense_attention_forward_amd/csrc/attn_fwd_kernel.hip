@@ -425,16 +425,30 @@ __device__ __forceinline__ void barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-#ifndef ATTN_PREFETCH
-#define ATTN_PREFETCH 4
-#endif
+// MFMA-phase settings per query-block count QB: LDS operand fragments in
+// flight, fragments that share one s_waitcnt, and whether the wave raises
+// its issue priority for the phase.
+//  * QB = 2: a wave waits for 4 fragments' reads at once, so 48 of the
+//    phase's 64 waits go away (every instruction a wave issues between its
+//    MFMAs delays the next one), with 6 in flight to keep 2 fragments' reads
+//    ahead of the group awaited; and it takes priority 1 for the phase (see
+//    the kernel loop). Measured +1-4% at 16K keys, +0-0.6% at 4K and 8K.
+//  * QB = 1: one wait per fragment, 4 in flight, no priority: its phase is
+//    bound by LDS reads (each fragment feeds one MFMA), and the settings
+//    above measured 1.2% slower there.
+template <int QB>
+struct MmaCfg {
+  static constexpr int kPrefetch = QB == 2 ? 6 : 4;
+  static constexpr int kWaitGroup = QB == 2 ? 4 : 1;
+  static constexpr bool kPrio = QB == 2;
+};
 
 // LDS reads of the MFMA phase are issued as inline assembly with explicit
 // s_waitcnt lgkmcnt(N): the compiler's own counting gives up (waits for
 // everything) as soon as the loop also holds direct-to-LDS loads, which
 // would drain the operand ring every few MFMAs. LDS reads of one wave
-// complete in issue order, so N = the number of reads issued after the one
-// awaited. A scheduling barrier after each wait keeps every use of the
+// complete in issue order, so N = the number of reads issued after the last
+// one awaited. A scheduling barrier after each wait keeps every use of the
 // awaited registers below it (naming them as in/out operands of the wait
 // did too, but made the hazard recognizer pad each MFMA with an s_nop);
 // volatile asm statements keep their order among themselves.
@@ -455,10 +469,11 @@ __device__ __forceinline__ void lgkm_wait() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// Ring of LDS operand fragments of an MFMA phase, ATTN_PREFETCH deep.
+// Ring of LDS operand fragments of an MFMA phase, PF deep.
+template <int PF>
 struct MmaRing {
-  u32x4 k[ATTN_PREFETCH];
-  u32x2 vlo[ATTN_PREFETCH], vhi[ATTN_PREFETCH];
+  u32x4 k[PF];
+  u32x2 vlo[PF], vhi[PF];
 };
 
 // ---------------------------------------------------------------------------
@@ -501,16 +516,18 @@ struct Frags16 {
   static constexpr int kV = BN / 4;         // V fragments: BN/32 steps x 8 d blocks
   static constexpr int kTotal = kV + kKB * 4;
   static constexpr int ops(int f) { return f < kV ? 2 : 1; }
-  static constexpr int after(int f, int pf) {
+  // LDS reads that may still be in flight when fragments f .. f + wg - 1
+  // must have landed, with fragments up to f + pf - 1 issued.
+  static constexpr int after(int f, int pf, int wg) {
     int n = 0;
-    for (int g = f + 1; g < f + pf && g < kTotal; ++g) n += ops(g);
+    for (int g = f + wg; g < f + pf && g < kTotal; ++g) n += ops(g);
     return n;
   }
 };
 
-template <int BN, int F>
-__device__ __forceinline__ void issue_frag16(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
-  constexpr int slot = F % ATTN_PREFETCH;
+template <int BN, int PF, int F>
+__device__ __forceinline__ void issue_frag16(MmaRing<PF>& ring, unsigned kaddr, unsigned vaddr) {
+  constexpr int slot = F % PF;
   if constexpr (F < Frags16<BN>::kV) {
     constexpr int db = F % 8, t = F / 8;
     constexpr int off = t * 8 * kVBlock + 256 * (db >> 1) + 32 * (db & 1);
@@ -523,15 +540,19 @@ __device__ __forceinline__ void issue_frag16(MmaRing& ring, unsigned kaddr, unsi
 }
 
 template <int BN, int QB, int F>
-__device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsigned vaddr,
+__device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring, unsigned kaddr, unsigned vaddr,
                                            const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                            const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
                                            f32x4 (&lacc)[QB], const bf16x8& ones) {
-  constexpr int slot = F % ATTN_PREFETCH;
-  constexpr int N = Frags16<BN>::after(F, ATTN_PREFETCH);
+  constexpr int PF = MmaCfg<QB>::kPrefetch, WG = MmaCfg<QB>::kWaitGroup;
+  static_assert(Frags16<BN>::kTotal % WG == 0 && WG < PF,
+                "fragments are awaited in whole groups, with reads of later ones in flight");
+  constexpr int slot = F % PF;
+  constexpr int N = Frags16<BN>::after(F, PF, WG);
+  constexpr bool wait = F % WG == 0;  // the first fragment of a group waits for all of it
   if constexpr (F < Frags16<BN>::kV) {
     constexpr int db = F % 8, t = F / 8;
-    lgkm_wait<N>();
+    if constexpr (wait) lgkm_wait<N>();
     const u32x4 a = __builtin_shufflevector(ring.vlo[slot], ring.vhi[slot], 0, 1, 2, 3);
     // In place through tied operands: each O accumulator keeps one register
     // set (with the builtin the allocator moved the accumulators between
@@ -550,7 +571,7 @@ __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsign
   } else {
     constexpr int f = F - Frags16<BN>::kV;
     constexpr int kb = f % Frags16<BN>::kKB, step = f / Frags16<BN>::kKB;
-    lgkm_wait<N>();
+    if constexpr (wait) lgkm_wait<N>();
     const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
     const f32x4 zero = {};
 #pragma unroll
@@ -558,16 +579,16 @@ __device__ __forceinline__ void mma_step16(MmaRing& ring, unsigned kaddr, unsign
       s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
                                                           0, 0, 0);
   }
-  if constexpr (F + ATTN_PREFETCH < Frags16<BN>::kTotal) issue_frag16<BN, F + ATTN_PREFETCH>(ring, kaddr, vaddr);
+  if constexpr (F + PF < Frags16<BN>::kTotal) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (F + 1 < Frags16<BN>::kTotal)
     mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
 }
 
-template <int BN, int F>
-__device__ __forceinline__ void issue_first16(MmaRing& ring, unsigned kaddr, unsigned vaddr) {
-  issue_frag16<BN, F>(ring, kaddr, vaddr);
-  if constexpr (F + 1 < ATTN_PREFETCH) issue_first16<BN, F + 1>(ring, kaddr, vaddr);
+template <int BN, int PF, int F>
+__device__ __forceinline__ void issue_first16(MmaRing<PF>& ring, unsigned kaddr, unsigned vaddr) {
+  issue_frag16<BN, PF, F>(ring, kaddr, vaddr);
+  if constexpr (F + 1 < PF) issue_first16<BN, PF, F + 1>(ring, kaddr, vaddr);
 }
 
 // MFMA phase i >= 1: the O rescale chosen by softmax phase i-1 (only if
@@ -596,8 +617,8 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
   }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
-  MmaRing ring;
-  issue_first16<BN, 0>(ring, kaddr, vaddr);
+  MmaRing<MmaCfg<QB>::kPrefetch> ring;
+  issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
   mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
   wait_mem();
   barrier();
@@ -913,11 +934,19 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   bool rescale;
   pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
                                 kept, thr, thr_gap);
+  constexpr bool kMfmaPrio = MmaCfg<QB>::kPrio;
+  // With two query blocks the wave in its MFMA phase gets the higher issue
+  // priority. Without it the SIMD favours the older wave (group A's), so
+  // while group A runs its softmax phase it delays group B's MFMAs: an
+  // instrumented copy measured group B's MFMA phase ~20% longer than group
+  // A's.
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
+    if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(1);
     pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
+    if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(0);
     if (i == ntiles) break;
     pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, thr, thr_gap);
@@ -949,6 +978,10 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #endif
 #ifndef ATTN_PP_MIN_WGS
 #define ATTN_PP_MIN_WGS 256
+#endif
+// PAIR256_EXP2EMU: one exponential in this many on the FMA pipe.
+#ifndef ATTN_EXP2_EMU_EVERY
+#define ATTN_EXP2_EMU_EVERY 4
 #endif
 
 
@@ -1019,10 +1052,9 @@ hipError_t launch(const Params& p, hipStream_t stream) {
   if (is_pair(p.variant)) {
     const int tiles = p.S / pair_rows(p.variant);
     const int npairs = (tiles + 1) / 2;
-    // PAIR256_EXP2EMU: one exponential in four on the FMA pipe
     auto kernel = p.variant == ATTN_VARIANT_PAIR256   ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, 0>
                   : p.variant == ATTN_VARIANT_PAIR128 ? attn_fwd_pingpong_kernel<ATTN_PP_BN, 1, 0>
-                                                      : attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, 4>;
+                                                      : attn_fwd_pingpong_kernel<ATTN_PP_BN, 2, ATTN_EXP2_EMU_EVERY>;
     return launch_kernel(kernel, dim3(nwg), dim3(2 * kThreads), stream, q, k, v, o, p.lse, p.S, tiles,
                          npairs, nwg, c);
   }
