@@ -504,10 +504,10 @@ struct MmaRing {
 //    both query blocks, so LDS traffic per FLOP is that of the four-wave
 //    kernel's 32x32x16 MFMAs (one fragment per 32x32 output block). With
 //    QB = 1 it doubles, and so do the LDS instructions a wave issues per
-//    MFMA. The two MFMAs of a fragment are issued back to back: the matrix
-//    pipe runs faster when consecutive MFMAs share their A operand (issuing
-//    a wait group's MFMAs query block by query block instead, so that the B
-//    operand repeats, measured 10% slower).
+//    MFMA. The two MFMAs of a fragment are issued back to back and the read
+//    that refills its ring slot right after them, so reads stay spread over
+//    the phase (issuing a wait group's MFMAs query block by query block,
+//    with the group's refills after all eight, measured 10% slower).
 // ---------------------------------------------------------------------------
 
 // Fragments of an MFMA phase in issue order: first the V fragments of
