@@ -6,7 +6,9 @@
 // scale*log2(e) folded into the score scale; the max is taken over raw
 // scores and scaled once), Chapter 11 (the O accumulator is rescaled only
 // when a row's max grows past a threshold, decided per wave; the article's
-// threshold is 8 in base-2 units, these kernels use 16, see kRebaseLog2),
+// threshold is 8 in base-2 units; the four-wave kernel uses 16, the
+// eight-wave kernel 32 against a raised base, see kRebaseLog2 and
+// kBitRebaseLog2),
 // Chapters 6-7 (K and V move through separate double buffers, and the
 // next tile's QK^T is issued while the current tile's softmax runs).
 //
@@ -50,6 +52,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -66,13 +69,24 @@ constexpr int kD = 128;         // head dimension
 constexpr int kBM = 128;        // query rows per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Rebase threshold in base-2 exponent units: a row keeps its base until its
-// max exceeds it by this much, so unnormalised P stays below 2^16 and O
-// below 2^16 * S * max|V| (fp32 overflows only for |V| beyond ~2^80). A
-// rescale of O costs 65 serial VALU instructions in the MFMA phase; 16
+// Rebase threshold of the four-wave kernel in base-2 exponent units: a row
+// keeps its base until its max exceeds it by this much, so unnormalised P
+// stays below 2^16 and O below 2^16 * S * max|V| (fp32 overflows only for
+// |V| beyond ~2^80). A rescale of O costs 65 serial VALU instructions; 16
 // instead of the article's 8 makes it rare on peaked rows (normal Q and K
 // of standard deviation 2 at S = 8192: from 17% of tiles per wave to 0.1%).
 constexpr float kRebaseLog2 = 16.0f;
+// Rebase threshold of the eight-wave kernel. Its kept base sits
+// kBitRebaseLog2 - 1 above the row's max * c at the row's last rebase, so
+// every P it computes is below 2 until some score passes the threshold,
+// and "P >= 2" is the top exponent bit of the bf16 P (pp_v_phase tests it
+// with one OR over all of a wave's P). O then stays below 2 * S * max|V|;
+// the price is at the small end: right after a rebase the largest P is
+// 2^-31, so products P * V fall below fp32's normal range once |V| is
+// under about 2^-95. 32 rather than 16 makes rebases rare on the 16K
+// outlier workload (from 16.9% of a wave's tiles to 3.7%), and a rebase
+// costs this kernel a second pass of exponentials.
+constexpr float kBitRebaseLog2 = 32.0f;
 
 // Tile parameters (compile-time): keys per K/V tile and the waves per SIMD
 // the register allocation is held to.
@@ -169,16 +183,18 @@ __device__ __forceinline__ void qk_tile(const char* ksm, int k_lane, const bf16x
 // error on [0, 1] (Remez exchange, with c0 pinned to 1 so integer arguments
 // are exact): 8.6e-5 with these float32 values, far below the 2^-9 of the
 // bf16 rounding that follows. They are produced by exp2_poly_fit.py beside
-// this file. The argument is clamped at -127 before it is split, so every
-// argument below -126 (any finite one, however large) gives at most
-// 2^-126, where the exponent unit gives 0; above, the lazy rescale keeps
-// arguments below the rebase threshold (16).
+// this file. The argument is clamped to [-127, 128] before it is split (one
+// v_med3), so every argument below -126 (any finite one, however large)
+// gives at most 2^-126, where the exponent unit gives 0, and every one from
+// 128 up, +Inf included, gives Inf. The P that the kernel keeps has
+// arguments below 1; the larger ones met before a rebase give at least 2 or
+// Inf, which set the exponent bit the rebase test reads.
 constexpr float kExp2C0 = 1.0f;
 constexpr float kExp2C1 = 0.6951163411140442f;
 constexpr float kExp2C2 = 0.22764700651168823f;
 constexpr float kExp2C3 = 0.07706519961357117f;
 __device__ __forceinline__ float exp2_poly(float x) {
-  const float xc = __builtin_fmaxf(x, -127.0f);
+  const float xc = __builtin_amdgcn_fmed3f(x, -127.0f, 128.0f);
   const float n = __builtin_floorf(xc);
   const float f = xc - n;
   float p = __builtin_fmaf(kExp2C3, f, kExp2C2);
@@ -498,16 +514,26 @@ struct MmaRing {
 //    32t + 16 + 4g + (j - 4) (j >= 4): exactly the keys the lane's two
 //    score blocks 2t and 2t+1 hold, so P needs no data movement. V^T is
 //    gathered for those keys with two ds_read_b64_tr_b16 per fragment.
-//  * The row sum is a 16x16x32 MFMA of an all-ones A with the same P
-//    operand: every row of its D is the key sum of lane l's query.
+//  * The row sum takes one v_smfmac_f32_16x16x64_bf16 per two steps: the B
+//    operand is the two steps' P side by side (64 keys), the sparse A is all
+//    ones and keeps, of each group of four k slots, slots {0, 1} in rows
+//    0-7 and {2, 3} in rows 8-15. Rows 0-7 of D (lanes 0-31) and rows 8-15
+//    (lanes 32-63) thus hold complementary halves of lane l's key sum,
+//    added once at the end. Half the matrix-pipe slots of a dense all-ones
+//    16x16x32 per step, at the same issue rate (17.1 ticks either way in a
+//    microbenchmark).
 //  * With QB = 2 every K and V fragment read from LDS feeds the MFMAs of
 //    both query blocks, so LDS traffic per FLOP is that of the four-wave
 //    kernel's 32x32x16 MFMAs (one fragment per 32x32 output block). With
 //    QB = 1 it doubles, and so do the LDS instructions a wave issues per
-//    MFMA. The two MFMAs of a fragment are issued back to back and the read
-//    that refills its ring slot right after them, so reads stay spread over
-//    the phase (issuing a wait group's MFMAs query block by query block,
-//    with the group's refills after all eight, measured 10% slower).
+//    MFMA. With QB = 2 the refill of a ring slot (fragment F + PF) is split
+//    around fragment F's two MFMAs: MFMA, read, MFMA, read (the one read of
+//    a K fragment goes between them). One LDS instruction between MFMAs
+//    costs a wave less than two back to back: in a microbenchmark of 4
+//    MFMA waves beside softmax waves PV fell from 19.45 to 18.61 ticks per
+//    MFMA, QK from 18.30 to 18.14. Issuing a wait group's MFMAs query block
+//    by query block, with the group's refills after all eight, measured 10%
+//    slower.
 // ---------------------------------------------------------------------------
 
 // Fragments of an MFMA phase in issue order: first the V fragments of
@@ -549,15 +575,34 @@ __device__ __forceinline__ void issue_frag16(MmaRing<PF>& ring, unsigned kaddr, 
   }
 }
 
+// Half of the refill of fragment F: part 0 is the first transposing read of
+// a V fragment or the one read of a K fragment, part 1 the second
+// transposing read (nothing for a K fragment).
+template <int BN, int PF, int F, int kPart>
+__device__ __forceinline__ void issue_half16(MmaRing<PF>& ring, unsigned kaddr, unsigned vaddr) {
+  constexpr int slot = F % PF;
+  if constexpr (F < Frags16<BN>::kV) {
+    constexpr int db = F % 8, t = F / 8;
+    constexpr int off = t * 8 * kVBlock + 256 * (db >> 1) + 32 * (db & 1) + kPart * 4 * kVBlock;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(kPart == 0 ? ring.vlo[slot] : ring.vhi[slot]) : "v"(vaddr), "i"(off));
+  } else if constexpr (kPart == 0) {
+    constexpr int f = F - Frags16<BN>::kV;
+    constexpr int kb = f % Frags16<BN>::kKB, step = f / Frags16<BN>::kKB;
+    ring.k[slot] = lds_b128<kb * 4 * kKBlockPair + step * 256>(kaddr);
+  }
+}
+
 template <int BN, int QB, int F>
 __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring, unsigned kaddr, unsigned vaddr,
                                            const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                            const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
-                                           f32x4 (&lacc)[QB], const bf16x8& ones) {
+                                           f32x4 (&lacc)[QB], const bf16x8& ones, int sidx) {
   constexpr int PF = MmaCfg<QB>::kPrefetch, WG = MmaCfg<QB>::kWaitGroup;
   static_assert(Frags16<BN>::kTotal % WG == 0 && WG < PF && (WG == 1 || WG == 4),
                 "fragments are awaited in whole groups, with reads of later ones in flight");
   constexpr int slot = F % PF;
+  constexpr bool kSplit = QB == 2 && F + PF < Frags16<BN>::kTotal;
   // the first fragment of a wait group waits for all of the group
   constexpr bool wait = Frags16<BN>::group_start(F, WG);
   constexpr int N = Frags16<BN>::after(F, PF, Frags16<BN>::group_len(F, WG));
@@ -569,15 +614,20 @@ __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring,
     // set (with the builtin the allocator moved the accumulators between
     // two sets every phase).
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][0]) : "v"(a), "v"(pf[0][t]));
-    if constexpr (QB == 2)
+    if constexpr (QB == 2) {
+      if constexpr (kSplit) issue_half16<BN, PF, F + PF, 0>(ring, kaddr, vaddr);
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][QB - 1]) : "v"(a), "v"(pf[QB - 1][t]));
-    if constexpr (db == 7) {
-      // Row sums of step t's P, the same rounded values the PV used. As
-      // builtins, so that the compiler's hazard checks cover any copy it
-      // makes of the operands.
+      if constexpr (kSplit) issue_half16<BN, PF, F + PF, 1>(ring, kaddr, vaddr);
+    }
+    if constexpr (db == 7 && t % 2 == 0) {
+      // Row sums of steps t and t+1's P (the same rounded values the PV
+      // uses), at the end of step t's fragments, while both are live.
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        lacc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[qb][t], lacc[qb], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        const bf16x16 b = __builtin_shufflevector(pf[qb][t], pf[qb][t + 1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                                  12, 13, 14, 15);
+        lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
+      }
     }
   } else {
     constexpr int f = F - Frags16<BN>::kV;
@@ -585,15 +635,20 @@ __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring,
     if constexpr (wait) lgkm_wait<N>();
     const bf16x8 a = __builtin_bit_cast(bf16x8, ring.k[slot]);
     const f32x4 zero = {};
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-      s[kb][qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[qb][step], step == 0 ? zero : s[kb][qb],
-                                                          0, 0, 0);
+    s[kb][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[0][step], step == 0 ? zero : s[kb][0], 0, 0, 0);
+    if constexpr (kSplit) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_half16<BN, PF, F + PF, 0>(ring, kaddr, vaddr);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (QB == 2)
+      s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][step], step == 0 ? zero : s[kb][1], 0, 0, 0);
+    if constexpr (kSplit) issue_half16<BN, PF, F + PF, 1>(ring, kaddr, vaddr);
   }
-  if constexpr (F + PF < Frags16<BN>::kTotal) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
+  if constexpr (!kSplit && F + PF < Frags16<BN>::kTotal) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (F + 1 < Frags16<BN>::kTotal)
-    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
+    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones, sidx);
 }
 
 template <int BN, int PF, int F>
@@ -611,7 +666,7 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
                                              const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                              const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
                                              const float (&alpha)[QB], bool rescale, f32x4 (&lacc)[QB],
-                                             const bf16x8& ones) {
+                                             const bf16x8& ones, int sidx) {
   if (rescale) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -630,7 +685,7 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing<MmaCfg<QB>::kPrefetch> ring;
   issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
-  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones);
+  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones, sidx);
   wait_mem();
   barrier();
 }
@@ -725,8 +780,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                              const char* lsrc, int ntiles, int fill, char* kfree,
                                              char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
                                              bf16x8 (&pf)[QB][BN / 32], float (&alpha)[QB],
-                                             bool& rescale, float (&kept)[QB], float (&thr)[QB],
-                                             float thr_gap) {
+                                             bool& rescale, float (&kept)[QB]) {
   constexpr int kTileBytes = BN * kD * 2;
   static_assert(Tiles<BN>::kLoadsPerWave == 8 && BN / 16 == 8, "load spread assumes 128-key tiles");
   // The two groups split the loads so that each phase pair moves one tile:
@@ -763,33 +817,18 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
     }
     __builtin_amdgcn_sched_barrier(0);
   };
-  // Base update with an early out: a row moves its base only when its raw
-  // max reaches `thr` = (kept + threshold) / c, which after the first tiles
-  // is rare, so the factor and the new base are computed only when some
-  // row of the wave needs them (a wave-uniform branch). Otherwise alpha
-  // keeps its stale value, which the MFMA phase does not read.
-  float raw[QB];
-  tile_max16<BN, QB>(s, raw);
-  bool need[QB];
-  uint64_t any = 0;  // one ballot per query block keeps the masks in SGPRs
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    need[qb] = raw[qb] >= thr[qb];
-    any |= __builtin_amdgcn_ballot_w64(need[qb]);
-  }
-  rescale = any != 0;
-  if (rescale) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m = raw[qb] * c;
-      alpha[qb] = need[qb] ? __builtin_amdgcn_exp2f(kept[qb] - m) : 1.0f;
-      kept[qb] = need[qb] ? m : kept[qb];
-      thr[qb] = need[qb] ? raw[qb] + thr_gap : thr[qb];
-    }
-  }
+  // Exponentials first, against the kept base, which sits kBitRebaseLog2 - 1
+  // above the row's max * c at its last rebase: P < 2 for every score below
+  // the threshold, so the top exponent bit of a bf16 P (P >= 2) flags a row
+  // that must rebase, overflow to Inf included. One OR over P's words tests
+  // the whole wave. Only when some row is flagged (a wave-uniform branch,
+  // rare after the first tile) are the row max, the new base and the factor
+  // alpha computed and P recomputed; this replaces the row max and compare
+  // that came before the exponentials on every tile. Otherwise alpha keeps
+  // its stale value, which the MFMA phase does not read. The empty assembly
+  // statements pin each part of P before the next loads (the compiler
+  // would otherwise sink all exponentials below them).
   issue2(0);
-  // The empty assembly statements pin each part of P before the next loads
-  // (the compiler would otherwise sink all exponentials below them).
   if constexpr (QB == 2) {
     exp16_part<BN, QB, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
     asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
@@ -808,6 +847,31 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
     issue2(4);
     issue2(6);
     exp16_part<BN, QB, kEmuEvery, 0, 6, 8>(s, c, kept, pf);
+  }
+  unsigned bits = 0;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+      const u32x4 w = __builtin_bit_cast(u32x4, pf[qb][t]);
+      bits |= w[0] | w[1] | w[2] | w[3];
+    }
+  rescale = __builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0u) != 0;
+  if (rescale) {
+    float raw[QB];
+    tile_max16<BN, QB>(s, raw);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m = __builtin_fmaf(raw[qb], c, kBitRebaseLog2 - 1.0f);
+      const bool need = m - kept[qb] >= kBitRebaseLog2;
+      alpha[qb] = need ? __builtin_amdgcn_exp2f(kept[qb] - m) : 1.0f;
+      kept[qb] = need ? m : kept[qb];
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (qb == 0) exp16_part<BN, QB, kEmuEvery, 0, 0, BN / 16>(s, c, kept, pf);
+      else exp16_part<BN, QB, kEmuEvery, QB - 1, 0, BN / 16>(s, c, kept, pf);
+    }
   }
   // P must be complete here, not computed after the barrier where it is
   // first used: the overlap of this phase with the other group's MFMAs
@@ -913,19 +977,23 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) acc[db][qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float kept[QB], thr[QB];
+  float kept[QB];
   f32x4 lacc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
+    // the first tile's exponentials against this base all overflow, so its
+    // P fails the bit test and every row takes the tile's max as its base
     kept[qb] = -FLT_MAX;
-    thr[qb] = -__builtin_inff();  // the first tile always sets the base
     lacc[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  const float thr_gap = kRebaseLog2 / c;
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
   asm volatile("" : "+v"(ones));  // keep it in registers, not rebuilt before each use
+  // sparse-A index of the row-sum smfmac: rows 0-7 (lanes 0-31 of D) keep
+  // the values k%4 in {0, 1} of each group of four, rows 8-15 keep {2, 3}
+  int sidx = (lane & 15) < 8 ? 0x4444 : 0xEEEE;
+  asm volatile("" : "+v"(sidx));
   f32x4 s[BN / 16][QB];
   bf16x8 pf[QB][BN / 32];
 #pragma unroll
@@ -944,7 +1012,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   float alpha[QB];
   bool rescale;
   pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
-                                kept, thr, thr_gap);
+                                kept);
   constexpr bool kMfmaPrio = MmaCfg<QB>::kPrio;
   // With two query blocks the wave in its MFMA phase gets the higher issue
   // priority. Without it the SIMD favours the older wave (group A's), so
@@ -956,18 +1024,21 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
     if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(1);
-    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones, sidx);
     if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(0);
     if (i == ntiles) break;
     pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
-                                  rescale, kept, thr, thr_gap);
+                                  rescale, kept);
   }
   if (group == 0) barrier();
 
   if (!valid) return;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float ltot = lacc[qb][0];
+    // the two row halves of D hold complementary halves of every key sum
+    const auto hs = __builtin_amdgcn_permlane32_swap(__float_as_uint(lacc[qb][0]), __float_as_uint(lacc[qb][0]),
+                                                     false, false);
+    const float ltot = __uint_as_float(hs[0]) + __uint_as_float(hs[1]);
     const float inv = 1.0f / ltot;
     const int qrow = qrow0 + 16 * qb;
     __bf16* orow = o + head + int64_t(qrow) * kD;

@@ -189,15 +189,20 @@ def test_dominant_key(daf):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-@pytest.mark.parametrize("direction", ["rising", "staircase", "falling", "late_spike"])
+@pytest.mark.parametrize("direction", ["rising", "staircase", "falling", "late_spike", "inf_spike"])
 def test_rebase_patterns(daf, direction, variant):
-    """Key-norm patterns for the lazy rescale at the kernels' threshold of
-    16 base-2 units. "rising" (a linear ramp) moves each row's base about
-    once after its first tile; "staircase" multiplies each 128-key tile's
-    norms by a growing step, so nearly every row moves its base on most
-    tiles (at least 4 times for 95% of rows, counted with the tile-by-tile
-    model at threshold 16 before the GPU runs); "falling" makes later P
-    flush to zero; a spike in the last tile forces one late, large rebase."""
+    """Key-norm patterns for the lazy rescale at the kernels' thresholds (16
+    base-2 units in the four-wave kernel, 32 in the eight-wave kernel, whose
+    test is the exponent bit of P against a raised base). "rising" (a linear
+    ramp) moves each row's base about once after its first tile; "staircase"
+    multiplies each 128-key tile's norms by a growing step, so nearly every
+    row moves its base on most tiles (at least 4 times for 95% of rows at
+    either threshold and tile length, counted with the tile-by-tile model
+    before the GPU runs); "falling" makes later P flush to zero; a spike in
+    the last tile forces one late, large rebase; "inf_spike" puts a key of
+    16 q_0 mid-sequence, about 260 base-2 units above query 0's base, so the
+    eight-wave kernel's first exponentials of that tile overflow to Inf
+    before its rebase test catches them."""
     from oracle import online_model
     from workloads import staircase_keys
     _say(f"case rebase {direction} variant={variant}")
@@ -208,17 +213,24 @@ def test_rebase_patterns(daf, direction, variant):
         k = (kf * torch.linspace(0.1, 8.0, S).reshape(1, 1, S, 1)).to(torch.bfloat16)
     elif direction == "staircase":
         k = staircase_keys(k)
-        for block_n in (64, 128):  # the key-tile lengths of the two kernels
+        # the key-tile lengths and thresholds of the two kernels
+        for block_n, thresh in ((64, 16.0), (128, 32.0)):
             stats = {}
-            online_model.online_attention(q, k, v, DEFAULT_SCALE, block_n=block_n, thresh_log2=16.0,
+            online_model.online_attention(q, k, v, DEFAULT_SCALE, block_n=block_n, thresh_log2=thresh,
                                           stats=stats)
             per_row = torch.cat(stats["row_rebases"]).float()
             assert (per_row >= 4).float().mean().item() >= 0.95
     elif direction == "falling":
         k = (kf * torch.linspace(8.0, 0.1, S).reshape(1, 1, S, 1)).to(torch.bfloat16)
-    else:
+    elif direction == "late_spike":
         kf[:, :, S - 5] = q.float()[:, :, 0] * 4.0
         k = kf.to(torch.bfloat16)
+    else:
+        kf[:, :, 700] = q.float()[:, :, 0] * 16.0
+        k = kf.to(torch.bfloat16)
+        c = float(torch.tensor(DEFAULT_SCALE, dtype=torch.float32)) * 1.4426950408889634
+        top = (q.float()[:, :, 0] * k.float()[:, :, 700]).sum(-1) * c
+        assert (top > 128 + 32).all()  # beyond float32 range against a base kept ~31 above the old max
     o, lse = _run(daf, q, k, v, variant=variant)
     o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
     _assert_parity(o, lse, o_ref, lse_ref, f"rebase {direction} v{variant}")
