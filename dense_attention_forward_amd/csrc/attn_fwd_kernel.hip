@@ -476,8 +476,12 @@ __device__ __forceinline__ u32x4 lds_b128(unsigned addr) {
 }
 template <int kOff0, int kOff1>
 __device__ __forceinline__ void lds_tr_pair(unsigned addr, u32x2& lo, u32x2& hi) {
+  // Early-clobber outputs: the second read takes its address after the
+  // first has been issued, so `lo` must not be given the address register
+  // (the first read may land before the second issues when the LDS queue
+  // is full).
   asm volatile("ds_read_b64_tr_b16 %0, %2 offset:%3\n\tds_read_b64_tr_b16 %1, %2 offset:%4"
-               : "=v"(lo), "=v"(hi) : "v"(addr), "i"(kOff0), "i"(kOff1));
+               : "=&v"(lo), "=&v"(hi) : "v"(addr), "i"(kOff0), "i"(kOff1));
 }
 template <int N>
 __device__ __forceinline__ void lgkm_wait() {
