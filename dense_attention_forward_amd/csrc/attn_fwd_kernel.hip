@@ -7,7 +7,7 @@
 // scores and scaled once), Chapter 11 (the O accumulator is rescaled only
 // when a row's max grows past a threshold, decided per wave; the article's
 // threshold is 8 in base-2 units; the four-wave kernel uses 16, the
-// eight-wave kernel 32 against a raised base, see kRebaseLog2 and
+// eight-wave kernel 48 against a raised base, see kRebaseLog2 and
 // kBitRebaseLog2),
 // Chapters 6-7 (K and V move through separate double buffers, and the
 // next tile's QK^T is issued while the current tile's softmax runs).
@@ -80,13 +80,14 @@ constexpr float kRebaseLog2 = 16.0f;
 // kBitRebaseLog2 - 1 above the row's max * c at the row's last rebase, so
 // every P it computes is below 2 until some score passes the threshold,
 // and "P >= 2" is the top exponent bit of the bf16 P (pp_v_phase tests it
-// with one OR over all of a wave's P). O then stays below 2 * S * max|V|;
-// the price is at the small end: right after a rebase the largest P is
-// 2^-31, so products P * V fall below fp32's normal range once |V| is
-// under about 2^-95. 32 rather than 16 makes rebases rare on the 16K
-// outlier workload (from 16.9% of a wave's tiles to 3.7%), and a rebase
-// costs this kernel a second pass of exponentials.
-constexpr float kBitRebaseLog2 = 32.0f;
+// with one OR over all of a wave's P). O then stays below 2 * S * max|V|.
+// The price is at the small end: right after a rebase the largest P is
+// 2^-47, so products P * V leave fp32's normal range once |V| is under
+// about 2^-79 (O keeps its absolute accuracy, not its relative one, for
+// such V). A rebase costs this kernel a second pass of exponentials; at 48
+// no row of the 4K-16K workloads rebases after its first tile (at 16, 16.9%
+// of a wave's tiles on the 16K outlier workload; at 32, 3.7%).
+constexpr float kBitRebaseLog2 = 48.0f;
 
 // Tile parameters (compile-time): keys per K/V tile and the waves per SIMD
 // the register allocation is held to.
@@ -442,21 +443,20 @@ __device__ __forceinline__ void barrier() {
 }
 
 // MFMA-phase settings per query-block count QB: LDS operand fragments in
-// flight, fragments that share one s_waitcnt, and whether the wave raises
-// its issue priority for the phase.
+// flight and fragments that share one s_waitcnt. (With either QB the wave
+// also raises its issue priority for the phase; see the kernel loop.)
 //  * QB = 2: a wave waits for 4 fragments' reads at once, so 48 of the
 //    phase's 64 waits go away (every instruction a wave issues between its
 //    MFMAs delays the next one), with 6 in flight to keep 2 fragments' reads
-//    ahead of the group awaited; and it takes priority 1 for the phase (see
-//    the kernel loop). Measured +1-4% at 16K keys, +0-0.6% at 4K and 8K.
-//  * QB = 1: one wait per fragment, 4 in flight, no priority: its phase is
-//    bound by LDS reads (each fragment feeds one MFMA), and the settings
-//    above measured 1.2% slower there.
+//    ahead of the group awaited. With the priority: +1-4% at 16K keys,
+//    +0-0.6% at 4K and 8K.
+//  * QB = 1: one wait per fragment and 4 in flight: its phase is bound by
+//    LDS reads (each fragment feeds one MFMA), and grouped waits with 6 in
+//    flight measured slower there.
 template <int QB>
 struct MmaCfg {
   static constexpr int kPrefetch = QB == 2 ? 6 : 4;
   static constexpr int kWaitGroup = QB == 2 ? 4 : 1;
-  static constexpr bool kPrio = QB == 2;
 };
 
 // LDS reads of the MFMA phase are issued as inline assembly with explicit
@@ -525,7 +525,10 @@ struct MmaRing {
 //    (lanes 32-63) thus hold complementary halves of lane l's key sum,
 //    added once at the end. Half the matrix-pipe slots of a dense all-ones
 //    16x16x32 per step, at the same issue rate (17.1 ticks either way in a
-//    microbenchmark).
+//    microbenchmark). The softmax wave issues them at the end of its phase,
+//    once P is complete (with its factor alpha applied to the sums first):
+//    that phase is now the shorter of the two, and the MFMA wave keeps only
+//    the 128 MFMAs of PV and QK.
 //  * With QB = 2 every K and V fragment read from LDS feeds the MFMAs of
 //    both query blocks, so LDS traffic per FLOP is that of the four-wave
 //    kernel's 32x32x16 MFMAs (one fragment per 32x32 output block). With
@@ -600,8 +603,7 @@ __device__ __forceinline__ void issue_half16(MmaRing<PF>& ring, unsigned kaddr, 
 template <int BN, int QB, int F>
 __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring, unsigned kaddr, unsigned vaddr,
                                            const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
-                                           const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
-                                           f32x4 (&lacc)[QB], const bf16x8& ones, int sidx) {
+                                           const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB]) {
   constexpr int PF = MmaCfg<QB>::kPrefetch, WG = MmaCfg<QB>::kWaitGroup;
   static_assert(Frags16<BN>::kTotal % WG == 0 && WG < PF && (WG == 1 || WG == 4),
                 "fragments are awaited in whole groups, with reads of later ones in flight");
@@ -623,16 +625,6 @@ __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring,
       asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc[db][QB - 1]) : "v"(a), "v"(pf[QB - 1][t]));
       if constexpr (kSplit) issue_half16<BN, PF, F + PF, 1>(ring, kaddr, vaddr);
     }
-    if constexpr (db == 7 && t % 2 == 0) {
-      // Row sums of steps t and t+1's P (the same rounded values the PV
-      // uses), at the end of step t's fragments, while both are live.
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const bf16x16 b = __builtin_shufflevector(pf[qb][t], pf[qb][t + 1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
-                                                  12, 13, 14, 15);
-        lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
-      }
-    }
   } else {
     constexpr int f = F - Frags16<BN>::kV;
     constexpr int kb = f % Frags16<BN>::kKB, step = f / Frags16<BN>::kKB;
@@ -652,7 +644,7 @@ __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring,
   if constexpr (!kSplit && F + PF < Frags16<BN>::kTotal) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
   if constexpr (F + 1 < Frags16<BN>::kTotal)
-    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones, sidx);
+    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc);
 }
 
 template <int BN, int PF, int F>
@@ -662,34 +654,33 @@ __device__ __forceinline__ void issue_first16(MmaRing<PF>& ring, unsigned kaddr,
 }
 
 // MFMA phase i >= 1: the O rescale chosen by softmax phase i-1 (only if
-// some row of the wave rebased), PV(i-1) and QK(i), then publish this
-// wave's finished loads and pass a barrier. The epilogue and the next
+// some row of the wave rebased; that phase already rescaled the row sums),
+// PV(i-1) and QK(i), then publish this wave's finished loads and pass a
+// barrier. The epilogue and the next
 // rescale read O long after its last MFMA (the QK steps follow it).
 template <int BN, int QB>
 __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                              const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                              const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
-                                             const float (&alpha)[QB], bool rescale, f32x4 (&lacc)[QB],
-                                             const bf16x8& ones, int sidx) {
+                                             const float (&alpha)[QB], bool rescale) {
   if (rescale) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) acc[db][qb] *= alpha[qb];
-      lacc[qb] *= alpha[qb];
     }
     // The PV MFMAs below are inline assembly, which the compiler's hazard
     // checks do not see: give the VALU writes their wait states here.
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
       asm volatile("s_nop 4" : "+v"(acc[0][qb]), "+v"(acc[1][qb]), "+v"(acc[2][qb]), "+v"(acc[3][qb]),
-                   "+v"(acc[4][qb]), "+v"(acc[5][qb]), "+v"(acc[6][qb]), "+v"(acc[7][qb]), "+v"(lacc[qb]));
+                   "+v"(acc[4][qb]), "+v"(acc[5][qb]), "+v"(acc[6][qb]), "+v"(acc[7][qb]));
   }
   const unsigned kaddr = unsigned(reinterpret_cast<uintptr_t>(ksm)) + unsigned(k_lane);
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing<MmaCfg<QB>::kPrefetch> ring;
   issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
-  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc, lacc, ones, sidx);
+  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc);
   wait_mem();
   barrier();
 }
@@ -784,7 +775,8 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                              const char* lsrc, int ntiles, int fill, char* kfree,
                                              char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
                                              bf16x8 (&pf)[QB][BN / 32], float (&alpha)[QB],
-                                             bool& rescale, float (&kept)[QB]) {
+                                             bool& rescale, float (&kept)[QB], f32x4 (&lacc)[QB],
+                                             const bf16x8& ones, int sidx) {
   constexpr int kTileBytes = BN * kD * 2;
   static_assert(Tiles<BN>::kLoadsPerWave == 8 && BN / 16 == 8, "load spread assumes 128-key tiles");
   // The two groups split the loads so that each phase pair moves one tile:
@@ -884,6 +876,20 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) asm volatile("" : "+v"(pf[qb][t]));
+  // Row sums of this tile's P (see the kernel comment), after the old sums
+  // take the factor of this tile's base update.
+  if (rescale) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) lacc[qb] *= alpha[qb];
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < BN / 32; t += 2) {
+      const bf16x16 b = __builtin_shufflevector(pf[qb][t], pf[qb][t + 1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                                12, 13, 14, 15);
+      lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
+    }
   if (group == 0) wait_vmem();
   barrier();
 }
@@ -904,9 +910,10 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 // stalled that phase for the whole transfer). Before the loop all eight
 // waves load K(0) and K(1).
 //
-// The MFMA phase also takes the row sum of the P it consumes, on the matrix
-// pipe; the softmax phase keeps the row max, the base update and the
-// exponentials.
+// The softmax phase computes P against the kept base, tests it for a
+// rebase (the row max and the base update run only when that test fires)
+// and takes P's row sums on the matrix pipe; the MFMA phase issues only
+// the MFMAs of PV and QK and their LDS reads.
 template <int BN, int QB, int kEmuEvery>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
@@ -1016,23 +1023,23 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   float alpha[QB];
   bool rescale;
   pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
-                                kept);
-  constexpr bool kMfmaPrio = MmaCfg<QB>::kPrio;
-  // With two query blocks the wave in its MFMA phase gets the higher issue
-  // priority. Without it the SIMD favours the older wave (group A's), so
-  // while group A runs its softmax phase it delays group B's MFMAs: an
-  // instrumented copy measured group B's MFMA phase ~20% longer than group
-  // A's.
+                                kept, lacc, ones, sidx);
+  // The wave in its MFMA phase gets the higher issue priority. Without it
+  // the SIMD favours the older wave (group A's), so while group A runs its
+  // softmax phase it delays group B's MFMAs: an instrumented copy measured
+  // group B's MFMA phase ~20% longer than group A's. It also keeps the
+  // softmax wave's row-sum MFMAs out of the MFMA wave's way (without it
+  // PAIR128 at s1k was 1.8% slower).
   for (int i = 1;; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
-    if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(1);
-    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, lacc, ones, sidx);
-    if constexpr (kMfmaPrio) __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_s_setprio(1);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
+    __builtin_amdgcn_s_setprio(0);
     if (i == ntiles) break;
     pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
-                                  rescale, kept);
+                                  rescale, kept, lacc, ones, sidx);
   }
   if (group == 0) barrier();
 

@@ -113,6 +113,12 @@ enum attn_variant {
  * relative. A caller that merges partial results by their lse (a split
  * over keys) sees the merge weights off by at most about 0.4%, the same
  * order as the bf16 rounding of o itself.
+ * Range. The PAIR variants keep each row's running base 47 base-2 units
+ * above the row max at its last move, so their unnormalised p lie in
+ * [2^-47, 2) for the largest key of a row: o cannot overflow for any
+ * finite v, but for |v| below about 2^-79 the fp32 products p * v leave
+ * the normal range and o keeps only its absolute accuracy. TILE128 keeps p
+ * in [1, 2^16) for that key instead.
  */
 ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S, int D, float scale, void* stream);

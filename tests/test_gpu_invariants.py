@@ -127,3 +127,24 @@ def test_affine_values(daf, variant):
     d = (o2 - want).abs()
     assert d.max().item() <= O_MAX and d.mean().item() <= O_MEAN
     assert torch.equal(l2, l1)  # the scores did not change, and the kernel is deterministic
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("e", [-64, 90])
+def test_value_scale_range(daf, variant, e):
+    """O is linear in V: scaling V by 2^e (exact in bf16) scales O by 2^e.
+    At 2^-64 the smallest nonzero value is 2^-67, above the 2^-79 from which
+    the raised base of the PAIR variants (largest p of a row down to 2^-47)
+    would push p * v below fp32's normal range; at 2^90 the largest is
+    2^92, where the TILE128 kernel's p of up to 2^16 summed over 640 keys
+    still fits fp32. Both keep O's relative accuracy."""
+    _say(f"case invariant V scale 2^{e} variant={variant}")
+    q, k, v = _inputs(507)
+    v2 = (v.float() * 2.0 ** e).to(torch.bfloat16)
+    assert torch.equal(v2.float(), v.float() * 2.0 ** e)
+    o1, l1 = _run(daf, q, k, v, variant)
+    o2, l2 = _run(daf, q, k, v2, variant)
+    _parity(o2 * 2.0 ** -e, l2, q, k, v, f"V scale 2^{e} v{variant}")
+    d = (o2 * 2.0 ** -e - o1).abs()
+    assert d.max().item() <= O_MAX and d.mean().item() <= O_MEAN
+    assert torch.equal(l2, l1)  # the scores did not change

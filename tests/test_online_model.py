@@ -110,7 +110,7 @@ def test_lazy_rescale_equals_two_pass(case, block_n):
     assert stats["max_p"] <= 2.0 ** 8 * (1 + 1e-12)
 
 
-@pytest.mark.parametrize("thresh", [0.0, 8.0, 15.0, 16.0, 32.0])
+@pytest.mark.parametrize("thresh", [0.0, 8.0, 15.0, 16.0, 48.0])
 def test_threshold_does_not_change_result(thresh):
     q, k, v = _ramp_inputs(384)
     o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, thresh_log2=thresh)
@@ -171,7 +171,7 @@ def test_rounded_rowsum_error_on_outlier_recipe():
 def test_staircase_rebases_repeatedly_at_the_kernels_thresholds():
     """The staircase key recipe of the GPU rebase tests (key norms rising
     tile by tile) makes nearly every row rebase on most tiles at the
-    kernels' thresholds, 16 for the four-wave kernel (64-key tiles) and 32
+    kernels' thresholds, 16 for the four-wave kernel (64-key tiles) and 48
     for the eight-wave kernel (128-key tiles), and at the other pairings too;
     the result still equals the two-pass oracle."""
     from workloads import staircase_keys
@@ -179,7 +179,7 @@ def test_staircase_rebases_repeatedly_at_the_kernels_thresholds():
     k = staircase_keys(k)
     o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
     for block_n in (64, 128):
-        for thresh in (16.0, 32.0):
+        for thresh in (16.0, 48.0):
             stats = {}
             o, lse = online_model.online_attention(q, k, v, DEFAULT_SCALE, block_n=block_n,
                                                    thresh_log2=thresh, stats=stats)

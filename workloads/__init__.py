@@ -136,7 +136,7 @@ def make_random(B: int, H: int, S: int, D: int, seed: int, qk_std: float = 1.0,
     return make_inputs(w)
 
 
-def staircase_keys(k: torch.Tensor, tile: int = 128, step: float = 14.0) -> torch.Tensor:
+def staircase_keys(k: torch.Tensor, tile: int = 128, step: float = 20.0) -> torch.Tensor:
     """K with its rows in key tile t (of `tile` keys) multiplied by
     0.25 + step * t, cast back to bf16: each tile's largest scores rise well
     above the previous tile's, so an online softmax moves its base on nearly
