@@ -770,7 +770,7 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float 
 // Softmax phase i: first this group's share of the tile loads (below), then
 // the row max and base update, whose factor for O (already holding
 // PV(i-1)) the next MFMA phase applies, and P(i).
-template <int BN, int QB, int kEmuEvery>
+template <int BN, int QB, int kEmuEvery, bool kFirst>
 __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                              const char* lsrc, int ntiles, int fill, char* kfree,
                                              char* vcur, float c, const f32x4 (&s)[BN / 16][QB],
@@ -824,35 +824,45 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // its stale value, which the MFMA phase does not read. The empty assembly
   // statements pin each part of P before the next loads (the compiler
   // would otherwise sink all exponentials below them).
-  issue2(0);
-  if constexpr (QB == 2) {
-    exp16_part<BN, QB, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
-    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
+  if constexpr (kFirst) {
+    // Every row rebases on its first tile (its base starts at -FLT_MAX), so
+    // the first phase goes straight to the row max.
+    issue2(0);
     issue2(2);
-    exp16_part<BN, QB, kEmuEvery, QB - 1, 0, 4>(s, c, kept, pf);
-    asm volatile("" : "+v"(pf[QB - 1][0]), "+v"(pf[QB - 1][1]));
     issue2(4);
     issue2(6);
-    exp16_part<BN, QB, kEmuEvery, QB - 1, 4, 8>(s, c, kept, pf);
+    rescale = true;
   } else {
-    exp16_part<BN, QB, kEmuEvery, 0, 0, 4>(s, c, kept, pf);
-    asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]));
-    issue2(2);
-    exp16_part<BN, QB, kEmuEvery, 0, 4, 6>(s, c, kept, pf);
-    asm volatile("" : "+v"(pf[0][2]));
-    issue2(4);
-    issue2(6);
-    exp16_part<BN, QB, kEmuEvery, 0, 6, 8>(s, c, kept, pf);
-  }
-  unsigned bits = 0;
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int t = 0; t < BN / 32; ++t) {
-      const u32x4 w = __builtin_bit_cast(u32x4, pf[qb][t]);
-      bits |= w[0] | w[1] | w[2] | w[3];
+    issue2(0);
+    if constexpr (QB == 2) {
+      exp16_part<BN, QB, kEmuEvery, 0, 0, 8>(s, c, kept, pf);
+      asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]), "+v"(pf[0][2]), "+v"(pf[0][3]));
+      issue2(2);
+      exp16_part<BN, QB, kEmuEvery, QB - 1, 0, 4>(s, c, kept, pf);
+      asm volatile("" : "+v"(pf[QB - 1][0]), "+v"(pf[QB - 1][1]));
+      issue2(4);
+      issue2(6);
+      exp16_part<BN, QB, kEmuEvery, QB - 1, 4, 8>(s, c, kept, pf);
+    } else {
+      exp16_part<BN, QB, kEmuEvery, 0, 0, 4>(s, c, kept, pf);
+      asm volatile("" : "+v"(pf[0][0]), "+v"(pf[0][1]));
+      issue2(2);
+      exp16_part<BN, QB, kEmuEvery, 0, 4, 6>(s, c, kept, pf);
+      asm volatile("" : "+v"(pf[0][2]));
+      issue2(4);
+      issue2(6);
+      exp16_part<BN, QB, kEmuEvery, 0, 6, 8>(s, c, kept, pf);
     }
-  rescale = __builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0u) != 0;
+    unsigned bits = 0;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int t = 0; t < BN / 32; ++t) {
+        const u32x4 w = __builtin_bit_cast(u32x4, pf[qb][t]);
+        bits |= w[0] | w[1] | w[2] | w[3];
+      }
+    rescale = __builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0u) != 0;
+  }
   if (rescale) {
     float raw[QB];
     tile_max16<BN, QB>(s, raw);
@@ -992,8 +1002,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   f32x4 lacc[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    // the first tile's exponentials against this base all overflow, so its
-    // P fails the bit test and every row takes the tile's max as its base
+    // every row takes its first tile's max as its base (alpha = 0 then)
     kept[qb] = -FLT_MAX;
     lacc[qb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -1022,7 +1031,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   barrier();
   float alpha[QB];
   bool rescale;
-  pp_v_phase<BN, QB, kEmuEvery>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
+  pp_v_phase<BN, QB, kEmuEvery, true>(0, group, wave, lsrc, ntiles, lfill, kb0, vb0, c, s, pf, alpha, rescale,
                                 kept, lacc, ones, sidx);
   // The wave in its MFMA phase gets the higher issue priority. Without it
   // the SIMD favours the older wave (group A's), so while group A runs its
@@ -1038,7 +1047,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
     __builtin_amdgcn_s_setprio(0);
     if (i == ntiles) break;
-    pp_v_phase<BN, QB, kEmuEvery>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
+    pp_v_phase<BN, QB, kEmuEvery, false>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, lacc, ones, sidx);
   }
   if (group == 0) barrier();
