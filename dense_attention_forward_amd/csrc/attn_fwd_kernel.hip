@@ -767,9 +767,10 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float 
     }
 }
 
-// Softmax phase i: first this group's share of the tile loads (below), then
-// the row max and base update, whose factor for O (already holding
-// PV(i-1)) the next MFMA phase applies, and P(i).
+// Softmax phase i: this group's share of the tile loads (below), spread
+// over P(i), the rebase test on P(i) (with the row max, the base update and
+// its factor alpha only when it fires; the next MFMA phase applies alpha to
+// O, which already holds PV(i-1)), then the row sums of P(i).
 template <int BN, int QB, int kEmuEvery, bool kFirst>
 __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                              const char* lsrc, int ntiles, int fill, char* kfree,
@@ -788,9 +789,11 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // The 4 waves of a group move 32 KB per phase through the CU's vector
   // memory path, and a wave's load issue stalls while that path is busy.
   // The wave's 8 loads are therefore spread over the phase instead of being
-  // issued up front: two after the base update, two after the first part of
-  // the exponentials and four after the second (measured 1-1.5% faster at
-  // 4K and 8K keys than starting two at the phase's start).
+  // issued up front: two at its start, two after the first query block's
+  // exponentials and four after half of the second's. (When the phase began
+  // with the row max, starting the loads before it was 1-1.5% slower at 4K
+  // and 8K keys; with the exponentials first, other spreads measured the
+  // same.)
   //
   // The loads go through a raw buffer resource over the one tile they
   // fetch (of K for group B, of V for group A, from `lsrc`), so that the
