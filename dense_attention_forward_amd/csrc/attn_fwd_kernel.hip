@@ -822,8 +822,8 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // that must rebase, overflow to Inf included. One OR over P's words tests
   // the whole wave. Only when some row is flagged (a wave-uniform branch,
   // rare after the first tile) are the row max, the new base and the factor
-  // alpha computed and P recomputed; this replaces the row max and compare
-  // that came before the exponentials on every tile. Otherwise alpha keeps
+  // alpha computed and P recomputed, so no tile pays for a row max before
+  // its exponentials. Otherwise alpha keeps
   // its stale value, which the MFMA phase does not read. The empty assembly
   // statements pin each part of P before the next loads (the compiler
   // would otherwise sink all exponentials below them).
