@@ -83,6 +83,33 @@ def test_small_shapes_full(daf, B, H, S, seed, std, vd, frac, variant):
     _assert_parity(o, lse, o_ref, lse_ref, f"small {B}x{H}x{S} v{variant}")
 
 
+def _random_cases(n=12, seed=4242):
+    """Seeded random shapes (S a multiple of 128 up to 2048, up to 6 heads in
+    all) with random input recipes: odd tile counts, ragged pair and XCD
+    tails, and every variant, beyond the hand-picked small shapes."""
+    g = torch.Generator().manual_seed(seed)
+    out = []
+    for c in range(n):
+        B = int(torch.randint(1, 3, (1,), generator=g))
+        H = int(torch.randint(1, 4, (1,), generator=g))
+        S = 128 * int(torch.randint(1, 17, (1,), generator=g))
+        std = [0.5, 1.0, 2.0][int(torch.randint(0, 3, (1,), generator=g))]
+        vd = ["normal", "uniform"][int(torch.randint(0, 2, (1,), generator=g))]
+        frac = [0.0, 0.01, 0.05][int(torch.randint(0, 3, (1,), generator=g))]
+        variant = VARIANTS[c % len(VARIANTS)]
+        out.append((B, H, S, 700 + c, std, vd, frac, variant))
+    return out
+
+
+@pytest.mark.parametrize("B,H,S,seed,std,vd,frac,variant", _random_cases())
+def test_random_shapes(daf, B, H, S, seed, std, vd, frac, variant):
+    _say(f"case random B={B} H={H} S={S} seed={seed} std={std} v={vd} outliers={frac} variant={variant}")
+    q, k, v = make_random(B, H, S, 128, seed=seed, qk_std=std, v_dist=vd, outlier_frac=frac)
+    o, lse = _run(daf, q, k, v, variant=variant)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, f"random {B}x{H}x{S} v{variant}")
+
+
 _REF = {}
 
 
