@@ -94,7 +94,12 @@ enum attn_variant {
  *   D       : head dimension, must be 128
  *   scale   : softmax scale applied to q.k, finite and > 0 (usually 1/sqrt(D));
  *             the kernels work in fp32 on scale * log2(e) * q.k, so every such
- *             product must be finite in fp32 (|scale * q.k| below about 2^127)
+ *             product must stay below 2^30 in magnitude (about 1e9): beyond
+ *             that, the fp32 rounding of a scaled score (its ulp exceeds 128
+ *             base-2 units) can push an exponent past the fp32 range and the
+ *             output becomes non-finite. Well below that limit, the fp32
+ *             rounding of the scores themselves already bounds the accuracy
+ *             of rows whose largest scores nearly tie.
  *   stream  : hipStream_t to enqueue on; NULL means the default stream
  * Inputs must be finite; NaN or Inf in q, k or v gives unspecified output.
  * Returns ATTN_OK or an error code; on error nothing is enqueued (except

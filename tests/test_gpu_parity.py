@@ -292,6 +292,26 @@ def test_other_scales(daf, scale):
     _assert_parity(o, lse, o_ref, lse_ref, f"scale {scale}")
 
 
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_huge_scores(daf, variant):
+    """Scores up to about 5e8, just inside the header's |scale * q.k| < 2^30
+    (q and k entries up to ~4e4): each row's softmax is all but one-hot, and
+    at this magnitude an fp32 score's ulp (up to 64 base-2 units) is larger
+    than the eight-wave kernel's 47-unit raised base, so its P may exceed 2
+    and it takes the rebase branch on such tiles. O must still be the
+    attended value row and lse the row max, to fp32 precision. (Beyond
+    2^30 the same rounding can overflow an exponent: the header's limit.)"""
+    _say(f"case huge scores variant={variant}")
+    q, k, v = make_random(1, 2, 512, 128, seed=28)
+    q = (q.float() * 1.0e4).to(torch.bfloat16)
+    k = (k.float() * 1.0e4).to(torch.bfloat16)
+    s = (q.double() @ k.double().transpose(-1, -2)) * DEFAULT_SCALE
+    assert 1e8 < s.abs().max().item() < 2.0 ** 30
+    o, lse = _run(daf, q, k, v, variant=variant)
+    o_ref, lse_ref = oracle.attention(q, k, v, DEFAULT_SCALE)
+    _assert_parity(o, lse, o_ref, lse_ref, f"huge scores v{variant}")
+
+
 def test_bad_arguments_raise(daf):
     _say("case bad arguments")
     dev = torch.device("cuda", 0)
