@@ -119,12 +119,14 @@ enum attn_variant {
  * over keys) sees the merge weights off by at most about 0.4%, the same
  * order as the bf16 rounding of o itself.
  * Range. The PAIR variants keep each row's running base 47 base-2 units
- * above the row max at its last move, so their unnormalised p stay below 2
- * (within the score limit above) and lie in [2^-47, 2) for the largest key
- * of a row: the fp32 accumulator of o stays below 2 * S * max|v|, and for
- * |v| below about 2^-79 the products p * v leave the normal range, where o
- * keeps only its absolute accuracy. TILE128 keeps p in [1, 2^16) for the
- * largest key, so its accumulator stays below 2^16 * S * max|v|.
+ * above the row max at its last move, so their unnormalised p lie in
+ * [2^-47, 2) for the largest key of a row while the fp32 ulp of the scaled
+ * scores is below that margin (|scale * q.k| below about 2^28), and below
+ * 2^17 up to the 2^30 limit: the fp32 accumulator of o stays below
+ * 2 * S * max|v| (2^17 * S * max|v| near the limit), and for |v| below about
+ * 2^-79 the products p * v leave the normal range, where o keeps only its
+ * absolute accuracy. TILE128 keeps p in [1, 2^16) for the largest key (up
+ * to 2^64 near the limit), so its accumulator stays below 2^16 * S * max|v|.
  */
 ATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int S, int D, float scale, void* stream);
