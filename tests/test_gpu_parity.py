@@ -283,7 +283,7 @@ def test_lse_bound_with_one_dominant_key(daf, variant):
     assert oerr.max().item() <= O_MAX and oerr.mean().item() <= O_MEAN
 
 
-@pytest.mark.parametrize("scale", [1.0, 0.25, 1e-3])
+@pytest.mark.parametrize("scale", [300.0, 1.0, 0.25, 1e-3, 1e-30])
 def test_other_scales(daf, scale):
     _say(f"case scale {scale}")
     q, k, v = make_random(1, 2, 256, 128, seed=27)
