@@ -656,13 +656,14 @@ __device__ __forceinline__ void issue_first16(MmaRing<PF>& ring, unsigned kaddr,
 // MFMA phase i >= 1: the O rescale chosen by softmax phase i-1 (only if
 // some row of the wave rebased; that phase already rescaled the row sums),
 // PV(i-1) and QK(i), then publish this wave's finished loads and pass a
-// barrier. The epilogue and the next
-// rescale read O long after its last MFMA (the QK steps follow it).
+// barrier (unless `nobarrier`: group B's last phase, which no phase of
+// group A waits for). The epilogue and the next rescale read O long after
+// its last MFMA (the QK steps follow it).
 template <int BN, int QB>
 __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                              const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                              const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
-                                             const float (&alpha)[QB], bool rescale) {
+                                             const float (&alpha)[QB], bool rescale, bool nobarrier) {
   if (rescale) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -682,6 +683,7 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
   issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
   mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc);
   wait_mem();
+  if (nobarrier) return;
   barrier();
 }
 
@@ -921,7 +923,15 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 // loaded by group A during its V(i) and awaited at its end. Each interval
 // thus moves one tile through the load path (issuing both in one phase
 // stalled that phase for the whole transfer). Before the loop all eight
-// waves load K(0) and K(1).
+// waves load K(0) and K(1), and each group its Q tile.
+//
+// All workgroups of a launch do equal work, so those of one round over the
+// CUs start and end together, and the Q reads at a round's start and the O
+// writes at its end come as bursts at the memory's bandwidth. Hence the first barrier waits
+// only for what group A's QK(0) needs (K(0) and A's Q), and at the end
+// group A stores its rows during group B's last MFMA phase, which ends
+// without a barrier (group A passes none after its own last phase, so the
+// counts match).
 //
 // The softmax phase computes P against the kept base, tests it for a
 // rebase (the row max and the base update run only when that test fires)
@@ -975,27 +985,37 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   const char* const lsrc = group == 1 ? kg : vg;
   const int lfill = group == 1 ? kfill : vfill;
 
-  {
 #pragma unroll
-    for (int i = 0; i < T::kBlocks / 8; ++i) {
-      const int j = 8 * i + wave8;
-      __builtin_amdgcn_global_load_lds(kg + j * 1024 + kfill, (lds_void*)(kb0 + j * kKBlockPair), 16, 0, 0);
-      if (ntiles > 1)
-        __builtin_amdgcn_global_load_lds(kg + kTileBytes + j * 1024 + kfill,
-                                         (lds_void*)(kb1 + j * kKBlockPair), 16, 0, 0);
-    }
+  for (int i = 0; i < T::kBlocks / 8; ++i) {
+    const int j = 8 * i + wave8;
+    __builtin_amdgcn_global_load_lds(kg + j * 1024 + kfill, (lds_void*)(kb0 + j * kKBlockPair), 16, 0, 0);
   }
 
   // Q fragments: query block qb, 32-dim step: dims 32*step + 8g .. +7.
   const int qrow0 = qt * (64 * QB) + wave * (16 * QB) + col;  // query of block 0; block qb is +16 qb
   bf16x8 qf[QB][4];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const uint4* qp = q + ((head + int64_t(qrow0 + 16 * qb) * kD) >> 3);
+    for (int qb = 0; qb < QB; ++qb) {
+      const uint4* qp = q + ((head + int64_t(qrow0 + 16 * qb) * kD) >> 3);
 #pragma unroll
-    for (int step = 0; step < 4; ++step) qf[qb][step] = __builtin_bit_cast(bf16x8, qp[4 * step + g]);
-  }
-
+      for (int step = 0; step < 4; ++step) qf[qb][step] = __builtin_bit_cast(bf16x8, qp[4 * step + g]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // K(1) is issued in every case (through a resource of zero length when
+  // there is no K(1): zero fills without a memory access), so that the wait
+  // counts below are fixed.
+  auto load_k1 = [&]() {
+    const __amdgpu_buffer_rsrc_t rs1 = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kg + kTileBytes), 0, ntiles > 1 ? kTileBytes : 0, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < T::kBlocks / 8; ++i) {
+      const int j = 8 * i + wave8;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs1, (lds_void*)(kb1 + j * kKBlockPair), 16, kfill, j * 1024, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
   f32x4 acc[8][QB];
 #pragma unroll
   for (int db = 0; db < 8; ++db)
@@ -1026,10 +1046,27 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
 #pragma unroll
       for (int e = 0; e < 8; ++e) pf[qb][t][e] = (__bf16)0.0f;
 
-  __syncthreads();
-  if (group == 1) barrier();
-
-  qk16_tile<BN, QB>(kb0, k_lane, qf, s);
+  // The first barrier needs K(0) only (and group A's Q, for its QK(0)
+  // right after): group A issues Q before K(1) and waits for all but K(1);
+  // group B, whose QK(0) comes one interval later, issues K(1) before its Q
+  // and waits for K(0) alone. Each group then runs its own copy of QK(0),
+  // so that the waits the compiler adds for Q stay on their own path.
+  static_assert(T::kBlocks / 8 == 4 && 4 + 4 * QB <= 15, "the prologue's wait counts");
+  if (group == 0) {
+    load_q();
+    load_k1();
+    __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0): K(0) and Q have landed
+    barrier();
+    qk16_tile<BN, QB>(kb0, k_lane, qf, s);
+  } else {
+    load_k1();
+    load_q();
+    // vmcnt(4 + 4 QB) lgkmcnt(0): K(0) has landed
+    __builtin_amdgcn_s_waitcnt(0x0070 | (4 + 4 * QB));
+    barrier();
+    barrier();
+    qk16_tile<BN, QB>(kb0, k_lane, qf, s);
+  }
   wait_mem();
   barrier();
   float alpha[QB];
@@ -1047,14 +1084,15 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
     __builtin_amdgcn_s_setprio(1);
-    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, i == ntiles && group == 1);
     __builtin_amdgcn_s_setprio(0);
     if (i == ntiles) break;
     pp_v_phase<BN, QB, kEmuEvery, false>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, lacc, ones, sidx);
   }
-  if (group == 0) barrier();
-
+  // Group B's last MFMA phase passed no barrier, and group A passes no
+  // extra one: the counts match, and each group stores its rows as soon as
+  // its own last phase is done (group A while group B runs its last one).
   if (!valid) return;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
