@@ -555,9 +555,9 @@ struct Frags16 {
   static constexpr int ops(int f) { return f < kV ? 2 : 1; }
   // LDS reads that may still be in flight when fragments f .. f + wg - 1
   // must have landed, with fragments up to f + pf - 1 issued.
-  static constexpr int after(int f, int pf, int wg) {
+  static constexpr int after(int f, int pf, int wg, int end = kTotal) {
     int n = 0;
-    for (int g = f + wg; g < f + pf && g < kTotal; ++g) n += ops(g);
+    for (int g = f + wg; g < f + pf && g < end; ++g) n += ops(g);
     return n;
   }
   // Fragments awaited together ("wait groups") with a group size of wg:
@@ -600,18 +600,18 @@ __device__ __forceinline__ void issue_half16(MmaRing<PF>& ring, unsigned kaddr, 
   }
 }
 
-template <int BN, int QB, int F>
+template <int BN, int QB, int F, int kEnd = Frags16<BN>::kTotal>
 __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring, unsigned kaddr, unsigned vaddr,
                                            const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                            const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB]) {
   constexpr int PF = MmaCfg<QB>::kPrefetch, WG = MmaCfg<QB>::kWaitGroup;
-  static_assert(Frags16<BN>::kTotal % WG == 0 && WG < PF && (WG == 1 || WG == 4),
+  static_assert(kEnd % WG == 0 && WG < PF && (WG == 1 || WG == 4),
                 "fragments are awaited in whole groups, with reads of later ones in flight");
   constexpr int slot = F % PF;
-  constexpr bool kSplit = QB == 2 && F + PF < Frags16<BN>::kTotal;
+  constexpr bool kSplit = QB == 2 && F + PF < kEnd;
   // the first fragment of a wait group waits for all of the group
   constexpr bool wait = Frags16<BN>::group_start(F, WG);
-  constexpr int N = Frags16<BN>::after(F, PF, Frags16<BN>::group_len(F, WG));
+  constexpr int N = Frags16<BN>::after(F, PF, Frags16<BN>::group_len(F, WG), kEnd);
   if constexpr (F < Frags16<BN>::kV) {
     constexpr int db = F % 8, t = F / 8;
     if constexpr (wait) lgkm_wait<N>();
@@ -641,10 +641,10 @@ __device__ __forceinline__ void mma_step16(MmaRing<MmaCfg<QB>::kPrefetch>& ring,
       s[kb][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[1][step], step == 0 ? zero : s[kb][1], 0, 0, 0);
     if constexpr (kSplit) issue_half16<BN, PF, F + PF, 1>(ring, kaddr, vaddr);
   }
-  if constexpr (!kSplit && F + PF < Frags16<BN>::kTotal) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
+  if constexpr (!kSplit && F + PF < kEnd) issue_frag16<BN, PF, F + PF>(ring, kaddr, vaddr);
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (F + 1 < Frags16<BN>::kTotal)
-    mma_step16<BN, QB, F + 1>(ring, kaddr, vaddr, qf, s, pf, acc);
+  if constexpr (F + 1 < kEnd)
+    mma_step16<BN, QB, F + 1, kEnd>(ring, kaddr, vaddr, qf, s, pf, acc);
 }
 
 template <int BN, int PF, int F>
@@ -657,9 +657,11 @@ __device__ __forceinline__ void issue_first16(MmaRing<PF>& ring, unsigned kaddr,
 // some row of the wave rebased; that phase already rescaled the row sums),
 // PV(i-1) and QK(i), then publish this wave's finished loads and pass a
 // barrier (unless `nobarrier`: group B's last phase, which no phase of
-// group A waits for). The epilogue and the next rescale read O long after
-// its last MFMA (the QK steps follow it).
-template <int BN, int QB>
+// group A waits for). The next rescale reads O long after its last MFMA
+// (the QK steps follow it). With kEnd = the V fragment count the phase
+// stops after PV: the last phase, which has no tile to score (the epilogue
+// reads O after its wait for the reads, long after the MFMAs issued).
+template <int BN, int QB, int kEnd = Frags16<BN>::kTotal>
 __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                              const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                              const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
@@ -681,7 +683,16 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing<MmaCfg<QB>::kPrefetch> ring;
   issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
-  mma_step16<BN, QB, 0>(ring, kaddr, vaddr, qf, s, pf, acc);
+  mma_step16<BN, QB, 0, kEnd>(ring, kaddr, vaddr, qf, s, pf, acc);
+  if constexpr (kEnd != Frags16<BN>::kTotal) {
+    // The epilogue's VALU instructions read O next, and the compiler's
+    // hazard checks do not see the MFMAs above (inline assembly): wait out
+    // an 8-pass MFMA's result latency (11 wait states) here.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      asm volatile("s_nop 7\n\ts_nop 3" : "+v"(acc[0][qb]), "+v"(acc[1][qb]), "+v"(acc[2][qb]), "+v"(acc[3][qb]),
+                   "+v"(acc[4][qb]), "+v"(acc[5][qb]), "+v"(acc[6][qb]), "+v"(acc[7][qb]));
+  }
   wait_mem();
   if (nobarrier) return;
   barrier();
@@ -803,7 +814,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // `fill` is fixed. They are issued in every phase: group B's last two
   // (K tiles ntiles and ntiles + 1) get a resource of zero length, so the
   // hardware's range check turns them into zero fills, without a memory
-  // access, of a K buffer that no later QK reads for a used score.
+  // access, of a K buffer that no QK reads.
   const bool kside = group == 1;
   const int tile = kside ? i + 2 : i;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
@@ -1079,17 +1090,23 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // group B's MFMA phase ~20% longer than group A's. It also keeps the
   // softmax wave's row-sum MFMAs out of the MFMA wave's way (without it
   // PAIR128 at s1k was 1.8% slower).
-  for (int i = 1;; ++i) {
+  for (int i = 1; i < ntiles; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
     __builtin_amdgcn_s_setprio(1);
-    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, i == ntiles && group == 1);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, false);
     __builtin_amdgcn_s_setprio(0);
-    if (i == ntiles) break;
     pp_v_phase<BN, QB, kEmuEvery, false>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, lacc, ones, sidx);
   }
+  // The last MFMA phase: PV(ntiles - 1) alone (there is no tile ntiles to
+  // score). Kept out of the loop: as a branch inside it, the second copy of
+  // the phase made the register allocator spill.
+  __builtin_amdgcn_s_setprio(1);
+  pp_m_phase<BN, QB, Frags16<BN>::kV>(ntiles & 1 ? kb1 : kb0, ntiles & 1 ? vb0 : vb1, k_lane, v_lane, qf, s, pf, acc,
+                                      alpha, rescale, group == 1);
+  __builtin_amdgcn_s_setprio(0);
   // Group B's last MFMA phase passed no barrier, and group A passes no
   // extra one: the counts match, and each group stores its rows as soon as
   // its own last phase is done (group A while group B runs its last one).

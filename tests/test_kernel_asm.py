@@ -6,8 +6,10 @@ then goes without the wait states the hardware needs, and the MFMA may read
 a stale value (this happened once with a constant operand the compiler
 rebuilt with v_mov right before each use). This test compiles the kernels to
 assembly and checks that no VALU instruction writes a register read by an
-inline-assembly MFMA within the next few instructions, and that the
-eight-wave kernels neither spill nor use scratch."""
+inline-assembly MFMA within the next few instructions, that no other
+instruction reads or writes an inline-assembly MFMA's result within the
+wait states its latency needs, and that the eight-wave kernels neither spill
+nor use scratch."""
 import re
 import subprocess
 from pathlib import Path
@@ -67,6 +69,40 @@ def _hazards(text: str):
     return found
 
 
+# Wait states between an 8-pass MFMA (v_mfma_f32_16x16x32_bf16) writing a
+# register and any other instruction reading or writing it.
+MFMA_RESULT_WAIT = 11
+
+
+def _wait_states(s: str) -> int:
+    m = re.fullmatch(r"s_nop\s+(\d+)", s)
+    return int(m.group(1)) + 1 if m else 1
+
+
+def _result_hazards(text: str):
+    """Inline-assembly MFMA results used by a non-MFMA instruction before
+    MFMA_RESULT_WAIT wait states have passed (in program order)."""
+    insts = list(_instructions(text))
+    found = []
+    for i, (in_asm, s) in enumerate(insts):
+        if not (in_asm and s.startswith("v_mfma")):
+            continue
+        dst = _regs(s.split(None, 1)[1].split(",")[0].strip())
+        waited = 0
+        for _, p in insts[i + 1:]:
+            if waited >= MFMA_RESULT_WAIT:
+                break
+            if not p.startswith("v_mfma") and not p.startswith("s_"):
+                parts = p.split(None, 1)
+                ops = [o.strip() for o in parts[1].split(",")] if len(parts) > 1 else []
+                used = set().union(set(), *(_regs(o) for o in ops))
+                if used & dst:
+                    found.append(f"{s}  ->  {p} after {waited} wait states")
+                    break
+            waited += _wait_states(p)
+    return found
+
+
 def test_checker_flags_a_planted_hazard():
     text = "\n".join(["\tv_mov_b32_e32 v10, s4", ";;#ASMSTART",
                       "\tv_mfma_f32_16x16x32_bf16 v[0:3], v[8:11], v[12:15], v[0:3]", ";;#ASMEND"])
@@ -74,6 +110,21 @@ def test_checker_flags_a_planted_hazard():
     text = "\n".join(["\tv_mov_b32_e32 v20, s4", ";;#ASMSTART",
                       "\tv_mfma_f32_16x16x32_bf16 v[0:3], v[8:11], v[12:15], v[0:3]", ";;#ASMEND"])
     assert _hazards(text) == []
+
+
+def test_result_checker_flags_an_early_read():
+    mfma = ["\t;;#ASMSTART", "\tv_mfma_f32_16x16x32_bf16 v[0:3], v[8:11], v[12:15], v[0:3]", "\t;;#ASMEND"]
+    early = mfma + ["\ts_nop 7", "\tv_mul_f32_e32 v20, v5, v2"]
+    assert len(_result_hazards("\n".join(early))) == 1
+    waited = mfma + ["\ts_nop 7", "\ts_nop 2", "\tv_mul_f32_e32 v20, v5, v2"]
+    assert _result_hazards("\n".join(waited)) == []
+    other = mfma + ["\tv_mul_f32_e32 v20, v5, v6"]
+    assert _result_hazards("\n".join(other)) == []
+
+
+def test_no_early_use_of_an_asm_mfma_result(tmp_path):
+    text = _asm(tmp_path)
+    assert _result_hazards(text) == []
 
 
 def test_no_valu_write_feeds_an_asm_mfma(tmp_path):
