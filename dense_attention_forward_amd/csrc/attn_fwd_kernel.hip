@@ -1120,12 +1120,31 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
     const float inv = 1.0f / ltot;
     const int qrow = qrow0 + 16 * qb;
     __bf16* orow = o + head + int64_t(qrow) * kD;
+    // Lane group g holds dims 16 db + 4g .. +3 of each block db. For the
+    // blocks 2p and 2p+1, one 16-lane swap between groups 2h and 2h+1 gives
+    // group 2h dims 16(2p) + 8h .. +7 and group 2h+1 dims 16(2p+1) + 8h .. +7:
+    // each lane stores 16 bytes, and a row's 64 bytes of the two blocks go
+    // out in one instruction.
+    const bool odd = g & 1;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      bf16x4 w;
+    for (int p = 0; p < 4; ++p) {
+      bf16x4 ca, cb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = (__bf16)(acc[db][qb][i] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 16 * db + 4 * g) = w;
+      for (int i = 0; i < 4; ++i) {
+        ca[i] = (__bf16)(acc[2 * p][qb][i] * inv);
+        cb[i] = (__bf16)(acc[2 * p + 1][qb][i] * inv);
+      }
+      const u32x2 a = __builtin_bit_cast(u32x2, ca), b = __builtin_bit_cast(u32x2, cb);
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        // [0]: a with groups 1 and 3 replaced by b of groups 0 and 2;
+        // [1]: b with groups 0 and 2 replaced by a of groups 1 and 3
+        const auto sw = __builtin_amdgcn_permlane16_swap(a[i], b[i], false, false);
+        w[i] = odd ? sw[0] : a[i];
+        w[2 + i] = odd ? b[i] : sw[1];
+      }
+      *reinterpret_cast<u32x4*>(orow + 32 * p + 16 * (g & 1) + 8 * (g >> 1)) = w;
     }
     if (g == 0) lse[int64_t(bh) * S + qrow] = (kept[qb] + __log2f(ltot)) * kLn2;
   }
