@@ -22,8 +22,9 @@
  *
  * Ownership: every pointer is a device pointer owned by the caller. The
  * library allocates nothing, keeps no state between calls and never
- * synchronises: attn_fwd enqueues one kernel on `stream` and returns.
- * q, k, v are only read; every element of o and lse is written.
+ * synchronises: attn_fwd enqueues one kernel on `stream` and returns, so a
+ * caller may also capture it into a HIP graph. q, k, v are only read;
+ * every element of o and lse is written.
  *
  * Errors: each function returns an attn_status code; nothing is printed
  * and nothing throws. A fault inside the kernel is reported by the HIP
