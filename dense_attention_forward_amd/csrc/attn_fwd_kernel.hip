@@ -927,9 +927,9 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 // SIMD it shares (the role split of Chapters 4 and 12, done here by
 // phase-shifting two groups of identical waves instead of specialised warps).
 //
-// Group A runs M(0) V(0) M(1) V(1) ... M(n); group B starts one barrier
-// later, so interval 2i+1 holds A's V(i) and B's M(i), interval 2i+2 A's
-// M(i+1) and B's V(i). K(i) and V(i) live in buffer i%2. K(i+2) is loaded
+// Group A runs M(0) V(0) M(1) V(1) ... M(n), where M(0) is QK(0) alone and
+// M(n) PV(n-1) alone; group B starts one barrier later, so interval 2i+1
+// holds A's V(i) and B's M(i), interval 2i+2 A's M(i+1) and B's V(i). K(i) and V(i) live in buffer i%2. K(i+2) is loaded
 // by group B during its V(i) and awaited at the end of its M(i+1); V(i) is
 // loaded by group A during its V(i) and awaited at its end. Each interval
 // thus moves one tile through the load path (issuing both in one phase
@@ -938,11 +938,11 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 //
 // All workgroups of a launch do equal work, so those of one round over the
 // CUs start and end together, and the Q reads at a round's start and the O
-// writes at its end come as bursts at the memory's bandwidth. Hence the first barrier waits
-// only for what group A's QK(0) needs (K(0) and A's Q), and at the end
-// group A stores its rows during group B's last MFMA phase, which ends
-// without a barrier (group A passes none after its own last phase, so the
-// counts match).
+// writes at its end come as bursts at the memory's bandwidth. Hence the
+// first barrier waits only for what group A's QK(0) needs (K(0) and A's Q),
+// and at the end group A stores its rows during group B's last MFMA phase,
+// which ends without a barrier (group A passes none after its own last
+// phase, so the counts match).
 //
 // The softmax phase computes P against the kept base, tests it for a
 // rebase (the row max and the base update run only when that test fires)
