@@ -908,6 +908,10 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lacc[qb] *= alpha[qb];
   }
+  // Above the MFMA wave's priority for these four: the matrix pipe takes
+  // them at once instead of after the other wave's stream, so this wave
+  // reaches the barrier sooner (+0.3-1.0% on the 4K-16K workloads).
+  __builtin_amdgcn_s_setprio(2);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -916,6 +920,7 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                                 12, 13, 14, 15);
       lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
     }
+  __builtin_amdgcn_s_setprio(0);
   if (group == 0) wait_vmem();
   barrier();
 }
