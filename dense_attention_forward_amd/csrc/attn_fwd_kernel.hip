@@ -836,10 +836,10 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   // the whole wave. Only when some row is flagged (a wave-uniform branch,
   // rare after the first tile) are the row max, the new base and the factor
   // alpha computed and P recomputed, so no tile pays for a row max before
-  // its exponentials. Otherwise alpha keeps
-  // its stale value, which the MFMA phase does not read. The empty assembly
-  // statements pin each part of P before the next loads (the compiler
-  // would otherwise sink all exponentials below them).
+  // its exponentials. Otherwise alpha keeps its stale value, which the MFMA
+  // phase does not read. The empty assembly statements pin each part of P
+  // before the next loads (the compiler would otherwise sink all
+  // exponentials below them).
   if constexpr (kFirst) {
     // Every row rebases on its first tile (its base starts at -FLT_MAX), so
     // the first phase goes straight to the row max.
