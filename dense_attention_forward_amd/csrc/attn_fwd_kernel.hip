@@ -525,10 +525,10 @@ struct MmaRing {
 //    (lanes 32-63) thus hold complementary halves of lane l's key sum,
 //    added once at the end. Half the matrix-pipe slots of a dense all-ones
 //    16x16x32 per step, at the same issue rate (17.1 ticks either way in a
-//    microbenchmark). The softmax wave issues them at the end of its phase,
-//    once P is complete (with its factor alpha applied to the sums first):
-//    that phase is now the shorter of the two, and the MFMA wave keeps only
-//    the 128 MFMAs of PV and QK.
+//    microbenchmark). The MFMA wave issues those of P(i-1) at the start of
+//    its phase, right after its first fragments' reads, whose latency they
+//    fill (the softmax phase before has already applied its factor alpha to
+//    the sums).
 //  * With QB = 2 every K and V fragment read from LDS feeds the MFMAs of
 //    both query blocks, so LDS traffic per FLOP is that of the four-wave
 //    kernel's 32x32x16 MFMAs (one fragment per 32x32 output block). With
@@ -655,6 +655,7 @@ __device__ __forceinline__ void issue_first16(MmaRing<PF>& ring, unsigned kaddr,
 
 // MFMA phase i >= 1: the O rescale chosen by softmax phase i-1 (only if
 // some row of the wave rebased; that phase already rescaled the row sums),
+// the row sums of P(i-1) while the first fragments' reads are in flight,
 // PV(i-1) and QK(i), then publish this wave's finished loads and pass a
 // barrier (unless `nobarrier`: group B's last phase, which no phase of
 // group A waits for). The next rescale reads O long after its last MFMA
@@ -665,7 +666,8 @@ template <int BN, int QB, int kEnd = Frags16<BN>::kTotal>
 __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int k_lane, int v_lane,
                                              const bf16x8 (&qf)[QB][4], f32x4 (&s)[BN / 16][QB],
                                              const bf16x8 (&pf)[QB][BN / 32], f32x4 (&acc)[8][QB],
-                                             const float (&alpha)[QB], bool rescale, bool nobarrier) {
+                                             const float (&alpha)[QB], bool rescale, bool nobarrier,
+                                             f32x4 (&lacc)[QB], const bf16x8& ones, int sidx) {
   if (rescale) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
@@ -683,6 +685,17 @@ __device__ __forceinline__ void pp_m_phase(const char* ksm, const char* vsm, int
   const unsigned vaddr = unsigned(reinterpret_cast<uintptr_t>(vsm)) + unsigned(v_lane);
   MmaRing<MmaCfg<QB>::kPrefetch> ring;
   issue_first16<BN, MmaCfg<QB>::kPrefetch, 0>(ring, kaddr, vaddr);
+  __builtin_amdgcn_sched_barrier(0);
+  // The row sums of P(i-1) while the first fragments' reads are in flight.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int t = 0; t < BN / 32; t += 2) {
+      const bf16x16 b = __builtin_shufflevector(pf[qb][t], pf[qb][t + 1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                                12, 13, 14, 15);
+      lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
+    }
+  __builtin_amdgcn_sched_barrier(0);
   mma_step16<BN, QB, 0, kEnd>(ring, kaddr, vaddr, qf, s, pf, acc);
   if constexpr (kEnd != Frags16<BN>::kTotal) {
     // The epilogue's VALU instructions read O next, and the compiler's
@@ -783,7 +796,8 @@ __device__ __forceinline__ void exp16_part(const f32x4 (&s)[BN / 16][QB], float 
 // Softmax phase i: this group's share of the tile loads (below), spread
 // over P(i), the rebase test on P(i) (with the row max, the base update and
 // its factor alpha only when it fires; the next MFMA phase applies alpha to
-// O, which already holds PV(i-1)), then the row sums of P(i).
+// O, which already holds PV(i-1)), and alpha applied to the row sums, which
+// hold P up to P(i-1) (the next MFMA phase adds those of P(i)).
 template <int BN, int QB, int kEmuEvery, bool kFirst>
 __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
                                              const char* lsrc, int ntiles, int fill, char* kfree,
@@ -902,25 +916,11 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) asm volatile("" : "+v"(pf[qb][t]));
-  // Row sums of this tile's P (see the kernel comment), after the old sums
-  // take the factor of this tile's base update.
+  // The row sums (up to P(i-1)) take the factor of this tile's base update.
   if (rescale) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) lacc[qb] *= alpha[qb];
   }
-  // Above the MFMA wave's priority for these four: the matrix pipe takes
-  // them at once instead of after the other wave's stream, so this wave
-  // reaches the barrier sooner (+0.3-1.0% on the 4K-16K workloads).
-  __builtin_amdgcn_s_setprio(2);
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int t = 0; t < BN / 32; t += 2) {
-      const bf16x16 b = __builtin_shufflevector(pf[qb][t], pf[qb][t + 1], 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
-                                                12, 13, 14, 15);
-      lacc[qb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(ones, b, lacc[qb], sidx, 0, 0);
-    }
-  __builtin_amdgcn_s_setprio(0);
   if (group == 0) wait_vmem();
   barrier();
 }
@@ -949,10 +949,10 @@ __device__ __forceinline__ void pp_v_phase(int i, int group, int wave,
 // which ends without a barrier (group A passes none after its own last
 // phase, so the counts match).
 //
-// The softmax phase computes P against the kept base, tests it for a
-// rebase (the row max and the base update run only when that test fires)
-// and takes P's row sums on the matrix pipe; the MFMA phase issues only
-// the MFMAs of PV and QK and their LDS reads.
+// The softmax phase computes P against the kept base and tests it for a
+// rebase (the row max and the base update run only when that test fires);
+// the MFMA phase issues the previous P's row sums (in the shadow of its
+// first reads) and the MFMAs of PV and QK with their LDS reads.
 template <int BN, int QB, int kEmuEvery>
 __global__ __launch_bounds__(2 * kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restrict__ k,
@@ -1092,15 +1092,13 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // The wave in its MFMA phase gets the higher issue priority. Without it
   // the SIMD favours the older wave (group A's), so while group A runs its
   // softmax phase it delays group B's MFMAs: an instrumented copy measured
-  // group B's MFMA phase ~20% longer than group A's. It also keeps the
-  // softmax wave's row-sum MFMAs out of the MFMA wave's way (without it
-  // PAIR128 at s1k was 1.8% slower).
+  // group B's MFMA phase ~20% longer than group A's.
   for (int i = 1; i < ntiles; ++i) {
     const bool odd = i & 1;
     char* const k_i = odd ? kb1 : kb0;
     char* const v_other = odd ? vb0 : vb1;
     __builtin_amdgcn_s_setprio(1);
-    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, false);
+    pp_m_phase<BN, QB>(k_i, v_other, k_lane, v_lane, qf, s, pf, acc, alpha, rescale, false, lacc, ones, sidx);
     __builtin_amdgcn_s_setprio(0);
     pp_v_phase<BN, QB, kEmuEvery, false>(i, group, wave, lsrc, ntiles, lfill, k_i, odd ? vb1 : vb0, c, s, pf, alpha,
                                   rescale, kept, lacc, ones, sidx);
@@ -1110,7 +1108,7 @@ void attn_fwd_pingpong_kernel(const uint4* __restrict__ q, const char* __restric
   // the phase made the register allocator spill.
   __builtin_amdgcn_s_setprio(1);
   pp_m_phase<BN, QB, Frags16<BN>::kV>(ntiles & 1 ? kb1 : kb0, ntiles & 1 ? vb0 : vb1, k_lane, v_lane, qf, s, pf, acc,
-                                      alpha, rescale, group == 1);
+                                      alpha, rescale, group == 1, lacc, ones, sidx);
   __builtin_amdgcn_s_setprio(0);
   // Group B's last MFMA phase passed no barrier, and group A passes no
   // extra one: the counts match, and each group stores its rows as soon as
